@@ -1,0 +1,111 @@
+"""Host-side allocator of physical KV blocks: a free list plus reference counts.
+
+Follows the allocator the pages describe:
+  * [nano-vllm blog §2.2]: a flat pool of ``num_blocks`` equal blocks, a free
+    list, ``allocate(n)`` that raises "KV cache block pool exhausted" when the
+    list is short, and ``free`` that returns blocks; a new block is taken only
+    once the tail block is full.
+  * [CANN notes §2.3]: ``ceil(prompt_len / block_size)`` blocks at prompt
+    time, one more block per decode append when the tail fills, all blocks
+    returned when the sequence ends.
+  * [vLLM notes, "引用计数与 LRU" / "块级共享"]: a block may be referenced by
+    several block tables; it goes back to the free list when its count drops
+    to zero.
+
+The free list starts as a seeded permutation of the block ids, so logical
+blocks land on scattered physical blocks (the [nano-vllm blog §2.2] point that
+blocks come back "in any order").  Which physical block an allocator returns
+is not fixed by the pages; outputs must not depend on it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+class PoolExhausted(RuntimeError):
+    """Raised when an allocation asks for more blocks than the free list holds."""
+
+
+def blocks_for_tokens(num_tokens: int, block_size: int) -> int:
+    """Blocks a sequence of ``num_tokens`` occupies: ceil(num_tokens / block_size)."""
+    return -(-int(num_tokens) // int(block_size))
+
+
+def full_blocks(num_tokens: int, block_size: int) -> int:
+    """Blocks completely filled by ``num_tokens`` tokens (only these are shareable
+    prefix blocks, [vLLM notes, "边界条件"]: 100 tokens -> 6 full blocks of 16)."""
+    return int(num_tokens) // int(block_size)
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int, rng: np.random.Generator | None = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        order = rng.permutation(self.num_blocks) if rng is not None else np.arange(self.num_blocks)
+        self.free_list: list[int] = [int(b) for b in order]
+        self.ref_count = np.zeros(self.num_blocks, dtype=np.int64)
+
+    # -- allocation ---------------------------------------------------------
+    @property
+    def num_free(self) -> int:
+        return len(self.free_list)
+
+    def allocate(self, n: int) -> list[int]:
+        n = int(n)
+        if n < 0:
+            raise ValueError("cannot allocate a negative number of blocks")
+        if n > len(self.free_list):
+            raise PoolExhausted("KV cache block pool exhausted")
+        blocks = self.free_list[:n]
+        del self.free_list[:n]
+        for b in blocks:
+            assert self.ref_count[b] == 0
+            self.ref_count[b] = 1
+        return blocks
+
+    def share(self, blocks: list[int]) -> list[int]:
+        """Attach already-allocated blocks to one more table (refcount + 1)."""
+        for b in blocks:
+            if self.ref_count[b] <= 0:
+                raise ValueError(f"block {b} is not allocated and cannot be shared")
+            self.ref_count[b] += 1
+        return list(blocks)
+
+    def free(self, blocks: list[int]) -> None:
+        """Drop one reference to each block; blocks reaching zero go back to the free list."""
+        for b in blocks:
+            if self.ref_count[b] <= 0:
+                raise ValueError(f"double free of block {b}")
+            self.ref_count[b] -= 1
+            if self.ref_count[b] == 0:
+                self.free_list.append(int(b))
+
+    # -- sequence helpers ---------------------------------------------------
+    def allocate_for_prompt(self, prompt_len: int) -> list[int]:
+        return self.allocate(blocks_for_tokens(prompt_len, self.block_size))
+
+    def grow_to(self, table: list[int], new_len: int) -> list[int]:
+        """Append blocks to ``table`` until it holds ``new_len`` tokens.
+
+        A new block is taken only when the current tail block is full; returns
+        the blocks added (empty when the tail still has room)."""
+        added: list[int] = []
+        while len(table) * self.block_size < new_len:
+            b = self.allocate(1)[0]
+            table.append(b)
+            added.append(b)
+        return added
+
+    def writable(self, block: int) -> bool:
+        """A block may be written only while exactly one table references it."""
+        return self.ref_count[block] == 1
+
+    def dump(self, tables: list[list[int]], lens: list[int]) -> str:
+        """Debug view: each sequence's table with the refcount of every block."""
+        lines = [f"free={self.num_free}/{self.num_blocks}"]
+        for s, (tab, n) in enumerate(zip(tables, lens)):
+            cells = " ".join(f"{b}(rc{int(self.ref_count[b])})" for b in tab)
+            lines.append(f"seq {s} len={n}: {cells}")
+        return "\n".join(lines)
