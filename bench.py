@@ -1,0 +1,290 @@
+"""Benchmark of the paged-decode hot path on one MI355X.
+
+One step = pa_cache_write (each sequence's newest token, t = len - 1) followed
+by pa_decode over the whole batch, with every input already resident in HBM.
+The KV pool is replicated R times (at least 2 GiB in all) and successive steps
+rotate through the copies, so each step reads its pool from HBM rather than
+from the 256 MB last-level cache.
+
+Prints one JSON line:
+  value       KV-read GB/s of the whole step (algorithmic bytes / step time)
+  roofline    the decode kernel's algorithmic bytes / its mean duration from
+              HIP events recorded around every launch in the timed region,
+              against the 8 TB/s HBM peak
+  cpu_baseline  the float64 CPU oracle on the same batch (1 BLAS thread)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama7b]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode KV-read GB/s (% of HBM peak) + decode tokens/s/layer, 1 GPU"
+ELEM = {"f16": 2, "bf16": 2, "fp8_e4m3": 1}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(b) -> dict:
+    """Bytes the step must move at minimum (valid tokens only, one layer)."""
+    lens = b.context_lens.astype(np.int64)
+    B, Hq, Hkv, D, bs = b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.block_size
+    kv = int(lens.sum()) * 2 * Hkv * D * ELEM[b.kv_dtype]
+    qo = B * Hq * D * (ELEM[b.q_dtype] * 2)
+    tables = 4 * int(np.sum(-(-lens // bs))) + 4 * B
+    decode = kv + qo + tables
+    write = B * 2 * Hkv * D * (ELEM[b.src_dtype] + ELEM[b.kv_dtype]) + 4 * B + 4 * B
+    unique_kv = b.unique_blocks_in_use() * 2 * bs * Hkv * D * ELEM[b.kv_dtype]
+    return {"kv": kv, "decode": decode, "write": write, "unique_kv_blocks": unique_kv}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(REPO, "paged_kv_cache_132_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(config: str, partition: int):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; otherwise None."""
+    path = os.path.join(REPO, "profiles", f"decode_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash() or rec.get("partition") != partition:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def build_workload(name: str):
+    from workloads import CONFIG_MAKERS
+
+    return CONFIG_MAKERS[name]()
+
+
+def upload(b, torch, pa, copies: int):
+    """Device tensors for the batch; `copies` replicas of the KV pool."""
+    dev = torch.device("cuda:0")
+
+    def d16(raw, dt):
+        t = torch.from_numpy(np.ascontiguousarray(raw).view(np.int16))
+        return t.view(torch.float16 if dt == "f16" else torch.bfloat16).to(dev)
+
+    bt = torch.from_numpy(b.block_table_array(pad=0)).to(dev)
+    lens = torch.from_numpy(b.context_lens.astype(np.int32)).to(dev)
+    q = d16(b.query, b.q_dtype)
+    new_k = d16(b.new_key[0], b.src_dtype)
+    new_v = d16(b.new_value[0], b.src_dtype)
+    if b.kv_dtype == "fp8_e4m3":
+        # Fill the fp8 pool through the cache write itself, one position at a
+        # time (prefill by repeated decode-step writes) from the generated
+        # pre-quantisation values.
+        src = d16(b.kv_source, b.src_dtype)
+        pool = torch.full(b.kv_source.shape, 0x7F, dtype=torch.uint8, device=dev)
+        L = lens.long()
+        for t in range(int(b.context_lens.max())):
+            blk = bt[:, t // b.block_size].long()
+            off = t % b.block_size
+            lens_t = torch.where(L > t, torch.full_like(lens, t + 1), torch.zeros_like(lens))
+            pa.cache_write(pool, src[blk, 0, off].contiguous(), src[blk, 1, off].contiguous(), bt, lens_t,
+                           b.k_scale, b.v_scale)
+        del src
+    else:
+        pool = d16(b.kv_pool, b.kv_dtype)
+    pools = [pool] + [pool.clone() for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    return {"bt": bt, "lens": lens, "q": q, "k": new_k, "v": new_v, "pools": pools}
+
+
+def cpu_baseline(b, budget_s: float = 20.0) -> dict:
+    """The oracle, as it stands, on a bounded sample: whole sequences of the
+    same batch, taken in order until about `budget_s` seconds are spent."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                      # pragma: no cover
+        threadpool_limits = None
+    bt = b.block_table_array()
+    lens = b.context_lens
+    if b.kv_dtype == "fp8_e4m3":
+        pool = None                          # encode only the sample's blocks below
+    else:
+        pool = b.kv_pool
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        done, tokens, t_total = [], 0, 0.0
+        order = list(range(b.num_seqs))
+        for s in order:
+            if b.kv_dtype == "fp8_e4m3":
+                blocks = sorted(set(b.tables[s]))
+                sub = oracle.encode_pool(b.kv_source[blocks], b.src_dtype, "fp8_e4m3", b.k_scale, b.v_scale)
+                remap = {blk: i for i, blk in enumerate(blocks)}
+                bt_s = np.array([[remap[x] for x in b.tables[s]]], dtype=np.int32)
+                t0 = time.perf_counter()
+                oracle.paged_decode(b.query[s:s + 1], b.q_dtype, sub, "fp8_e4m3", bt_s, lens[s:s + 1],
+                                    b.block_size, b.scale, b.k_scale, b.v_scale)
+                t_total += time.perf_counter() - t0
+            else:
+                t0 = time.perf_counter()
+                oracle.paged_decode(b.query[s:s + 1], b.q_dtype, pool, b.kv_dtype, bt[s:s + 1], lens[s:s + 1],
+                                    b.block_size, b.scale)
+                t_total += time.perf_counter() - t0
+            done.append(s)
+            tokens += int(lens[s])
+            if t_total >= budget_s:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    kv_bytes = tokens * 2 * b.num_kv_heads * b.head_dim * ELEM[b.kv_dtype]
+    return {
+        "value": round(kv_bytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(done)} of {b.num_seqs} sequences ({tokens} context tokens) of the same batch, "
+                  f"float64 numpy decode, {t_total:.1f} s",
+        "tokens_per_s_per_layer": round(len(done) / t_total, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama7b")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
+              f"single-GPU and shards by sequence or KV head without communication.", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_132_amd as pa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pa.load()
+    log(f"building workload {args.config}")
+    b = build_workload(args.config)
+    nbytes = algorithmic_bytes(b)
+    pool_bytes = b.num_blocks * 2 * b.block_size * b.num_kv_heads * b.head_dim * ELEM[b.kv_dtype]
+    copies = max(2, math.ceil((2 << 30) / pool_bytes))
+    log(f"uploading: pool {pool_bytes / 2**20:.0f} MiB x {copies} copies")
+    dev = upload(b, torch, pa, copies)
+    kvt = pa.pa_dtype(dev["pools"][0])
+    mb = b.max_blocks_per_seq
+    partition = pa.decode_partition_size(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.block_size,
+                                         mb, kvt, args.partition_size)
+    ws = torch.zeros(pa.decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim,
+                                              b.block_size, mb, kvt, args.partition_size),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dev["q"])
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        pool = dev["pools"][i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        pa.cache_write(pool, dev["k"], dev["v"], dev["bt"], dev["lens"], b.k_scale, b.v_scale)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.decode(dev["q"], pool, dev["bt"], dev["lens"], b.scale, b.k_scale, b.v_scale, out=out,
+                  workspace=ws, partition_size=args.partition_size)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    write_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    ms_step = wall * 1e3 / args.steps
+    dec_us = float(decode_ms.mean() * 1e3)
+    achieved = nbytes["decode"] / (dec_us * 1e-6) / 1e9
+    step_bytes = nbytes["decode"] + nbytes["write"]
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"decode mean {dec_us:.1f} us (p10 {np.percentile(decode_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(decode_ms, 90) * 1e3:.1f}); write mean {write_ms.mean() * 1e3:.1f} us; "
+        f"step {ms_step * 1e3:.1f} us")
+    traffic = counter_traffic(args.config, partition)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": b.name, "num_seqs": b.num_seqs, "num_heads": b.num_heads,
+            "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
+            "q_dtype": b.q_dtype, "kv_dtype": b.kv_dtype, "context_tokens": int(b.context_lens.sum()),
+            "seed": b.seed, "partition_size": partition, "pool_copies": copies,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s_per_layer": round(b.num_seqs / (ms_step * 1e-3), 1),
+        "decode_kernel_us": round(dec_us, 2),
+        "write_kernel_us": round(float(write_ms.mean() * 1e3), 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "algorithmic_bytes": nbytes,
+    }
+    if b.notes.get("prefix_blocks"):
+        res["unique_kv_gbs"] = round(nbytes["unique_kv_blocks"] / (dec_us * 1e-6) / 1e9, 1)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

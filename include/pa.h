@@ -1,0 +1,180 @@
+/*
+ * pa.h -- paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Two operations, both defined by the
+ * three web pages on paged KV caches this library follows:
+ *
+ *   [nano-vllm blog]  2kiu.com/news/6344849 -- "PagedAttention and prefix
+ *                     caching", reproduced with nano-vllm (sections 1-7)
+ *   [vLLM notes]      "vLLM: PagedAttention 与前缀缓存" (personal-site-7tw.pages.dev)
+ *   [CANN notes]      discosf.com/news/6244710 -- Paged KV Cache and Packed
+ *                     Sequence in cann-recipes-infer (sections 1-6)
+ *
+ * Data layout shared by both calls (all tensors contiguous, row-major):
+ *   kv_pool       [num_blocks, 2, block_size, num_kv_heads, head_dim]
+ *                 index 1 is 0 for K, 1 for V        ([CANN notes §2.1])
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entry j of row s is
+ *                 the physical block holding logical block j of sequence s
+ *                 ([nano-vllm blog §2.2], [CANN notes §2.2]); entries past
+ *                 ceil(len / block_size) are never read
+ *   context_lens  int32 [num_seqs]: tokens in each sequence
+ *   Token t of sequence s lives in block block_tables[s][t / block_size] at
+ *   offset t % block_size ([CANN notes §2.2]).
+ *
+ * Element types (pa_dtype):
+ *   PA_F16       IEEE binary16
+ *   PA_BF16      bfloat16
+ *   PA_FP8_E4M3  OCP fp8 E4M3 (bias 7, max 448, no infinities, 0x7F/0xFF NaN);
+ *                a stored code c stands for value(c) * scale, with one fp32
+ *                scale for all of K (k_scale) and one for all of V (v_scale).
+ *                ([nano-vllm blog §1.1, §6.3] name fp8 KV; the encoding is
+ *                the OCP one.)
+ *
+ * Pointers: every pointer is device memory owned by the caller, 16-byte
+ * aligned, and stays valid until the work enqueued on `stream` completes.
+ * The library allocates nothing and keeps no per-call state.  `stream` is a
+ * hipStream_t (NULL = the default stream); every call only enqueues work on
+ * it and returns without waiting.
+ *
+ * Errors: each call checks its arguments on the host before enqueueing
+ * anything and returns a status; nothing is thrown across the ABI.  What the
+ * host cannot check is the caller's contract: block-table entries that are
+ * read must lie in [0, num_blocks), lengths must not exceed
+ * max_blocks_per_seq * block_size, write slots must be distinct, and no write
+ * may target a block that another table also references (shared blocks are
+ * read-only, [nano-vllm blog §4.3]).  The kernels do not fault on a broken
+ * contract: a block id outside the pool is skipped (its tokens are left out
+ * of attention, its write is dropped) and a longer length is cut to
+ * max_blocks_per_seq * block_size -- the results are then meaningless, but
+ * memory outside the arguments is never touched.
+ *
+ * Supported: head_dim 64 or 128; block_size 16 or 32; num_heads a multiple
+ * of num_kv_heads with num_heads / num_kv_heads in {1, 2, 4, 8} (query head h
+ * reads KV head h / (num_heads / num_kv_heads)); (query, kv) dtypes
+ * (F16, F16), (BF16, BF16) and (BF16, FP8_E4M3).  Other combinations return
+ * PA_ERR_UNSUPPORTED.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL                     */
+    PA_ERR_BAD_SHAPE = 2,           /* a size is out of range or inconsistent         */
+    PA_ERR_BAD_DTYPE = 3,           /* a dtype value is not a pa_dtype                */
+    PA_ERR_UNSUPPORTED = 4,         /* valid but not implemented combination          */
+    PA_ERR_MISALIGNED = 5,          /* a pointer is not 16-byte aligned               */
+    PA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes < pa_decode_workspace_size()   */
+    PA_ERR_HIP = 7                  /* the HIP runtime rejected a launch              */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F16 = 0,
+    PA_BF16 = 1,
+    PA_FP8_E4M3 = 2
+} pa_dtype;
+
+/*
+ * pa_cache_write -- store each sequence's newest token into the paged pool
+ * (the per-token KV write of [nano-vllm blog §4.1 step 3] and
+ * [CANN notes §4.3 steps 1-3], vLLM's reshape_and_cache).
+ *
+ * For every sequence s with L = context_lens[s] > 0 (the length AFTER the new
+ * token was appended), with t = L - 1, b = block_tables[s][t / block_size],
+ * o = t % block_size:
+ *     kv_pool[b][0][o][g][:] = enc(key[s][g][:])
+ *     kv_pool[b][1][o][g][:] = enc(value[s][g][:])      for every KV head g
+ * enc is a bit copy when src_dtype == kv_dtype; for PA_FP8_E4M3 it is
+ * e4m3(float32(x) / k_scale) (v_scale for V): IEEE float32 division, round
+ * to nearest with ties to even, magnitudes beyond 448 saturate to 448, NaN
+ * stays NaN.  A sequence with context_lens[s] <= 0 writes nothing.  The block
+ * holding slot t must already be in the table: allocating it when the tail
+ * block is full is the host's job ([CANN notes §2.3], [nano-vllm blog §2.2]).
+ *
+ *   kv_pool       in/out  [num_blocks, 2, block_size, num_kv_heads, head_dim] of kv_dtype
+ *   key, value    in      [num_seqs, num_kv_heads, head_dim] of src_dtype
+ *   (src, kv) dtypes: (F16, F16), (BF16, BF16), (BF16, FP8_E4M3), (F16, FP8_E4M3)
+ *   k_scale, v_scale      used only for FP8_E4M3; must then be finite and > 0
+ */
+pa_status pa_cache_write(void* kv_pool, pa_dtype kv_dtype,
+                         const void* key, const void* value, pa_dtype src_dtype,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                         float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode_partition_size -- tokens per split-K partition pa_decode will use
+ * for these arguments.  `requested` 0 lets the library choose; a positive
+ * multiple of block_size is taken as given.  Returns 0 for invalid arguments.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, pa_dtype kv_dtype,
+                                 int32_t requested);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs with
+ * the same arguments (same `partition_size`).  Returns 0 for invalid
+ * arguments.  The workspace holds per-partition partial results and one
+ * arrival counter per (sequence, KV-head group).
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                int32_t max_blocks_per_seq, pa_dtype kv_dtype,
+                                int32_t partition_size);
+
+/*
+ * pa_decode -- one decode step of paged attention ([nano-vllm blog §2.3],
+ * [CANN notes §4.3 step 4]).  For each sequence s with L = context_lens[s]
+ * and each query head h, with g = h / (num_heads / num_kv_heads):
+ *     z_t   = scale * k_scale * <query[s][h], K_t[g]>      t = 0 .. L-1
+ *     p     = softmax(z)
+ *     out[s][h] = v_scale * sum_t p_t * V_t[g]
+ * where K_t / V_t are read through the block table; slots of the last block
+ * at or beyond L are excluded (the tail mask of [nano-vllm blog §2.3]).  A
+ * sequence with L <= 0 gets a zero output.  k_scale / v_scale apply to
+ * FP8_E4M3 KV only (pass 1 otherwise).  The result is rounded to q_dtype
+ * (nearest, ties to even) from float32 accumulation.
+ *
+ *   out           out     [num_seqs, num_heads, head_dim] of q_dtype
+ *   query         in      [num_seqs, num_heads, head_dim] of q_dtype
+ *   kv_pool       in      [num_blocks, 2, block_size, num_kv_heads, head_dim] of kv_dtype
+ *   partition_size        0 = library choice, else a positive multiple of block_size:
+ *                         tokens per split-K partition (a sequence shorter than one
+ *                         partition is not split)
+ *   workspace     in/out  device memory of at least pa_decode_workspace_size(...) bytes.
+ *                         It must be zero-filled before its first use; every call that
+ *                         completes leaves it zero-filled again where it matters (the
+ *                         arrival counters), so one zeroed workspace serves any number
+ *                         of successive calls.  Calls that may run concurrently need
+ *                         separate workspaces.
+ *
+ * The pass is a single kernel: workgroups own (sequence, group of KV heads,
+ * partition); the last workgroup of a sequence to finish merges the
+ * partitions' partial softmax states.  Output does not depend on which
+ * physical blocks the table names, only on their logical order.
+ */
+pa_status pa_decode(void* out, const void* query, pa_dtype q_dtype,
+                    const void* kv_pool, pa_dtype kv_dtype,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                    float scale, float k_scale, float v_scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status value (static storage, never NULL). */
+const char* pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,29 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+The hot path is a C-ABI library (libpa.so, hand-written HIP kernels, declared
+in include/pa.h); this package is its thin Python binding:
+
+    cache_write(kv_pool, key, value, block_tables, context_lens, k_scale, v_scale)
+    decode(query, kv_pool, block_tables, context_lens, scale, k_scale, v_scale, ...)
+
+Build the library with ``python -m paged_kv_cache_132_amd.build``.
+"""
+from ._lib import (
+    PA_BF16,
+    PA_F16,
+    PA_FP8_E4M3,
+    EXPORTED,
+    LIB_PATH,
+    Workspace,
+    cache_write,
+    decode,
+    decode_partition_size,
+    decode_workspace_size,
+    load,
+    pa_dtype,
+)
+
+__all__ = [
+    "PA_F16", "PA_BF16", "PA_FP8_E4M3", "EXPORTED", "LIB_PATH", "Workspace", "cache_write", "decode",
+    "decode_partition_size", "decode_workspace_size", "load", "pa_dtype",
+]

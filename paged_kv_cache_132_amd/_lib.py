@@ -1,0 +1,181 @@
+"""ctypes binding of libpa.so: argument marshalling only.
+
+Every function takes torch tensors that already live on a HIP device, checks
+that their shapes agree with each other, and passes raw device pointers plus
+sizes to the C ABI on torch's current stream.  All arithmetic runs in the HIP
+kernels; a missing or unloadable library raises instead of falling back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+STATUS_NAMES = {
+    0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
+    4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_MISALIGNED", 6: "PA_ERR_WORKSPACE_TOO_SMALL", 7: "PA_ERR_HIP",
+}
+EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_decode_partition_size",
+            "pa_status_string")
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load() -> ctypes.CDLL:
+    """Load libpa.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_132_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        i32, f32, vp, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        lib.pa_cache_write.restype = ctypes.c_int
+        lib.pa_cache_write.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp,
+                                       i32, i32, i32, i32, i32, i32, f32, f32, vp]
+        lib.pa_decode.restype = ctypes.c_int
+        lib.pa_decode.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                  i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
+                                  vp, sz, vp]
+        lib.pa_decode_workspace_size.restype = sz
+        lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
+        lib.pa_decode_partition_size.restype = i32
+        lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
+        lib.pa_status_string.restype = ctypes.c_char_p
+        lib.pa_status_string.argtypes = [ctypes.c_int]
+        _lib = lib
+        return lib
+
+
+def pa_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return PA_F16
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        name = load().pa_status_string(status).decode()
+        raise RuntimeError(f"{what} failed: {name}")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _pool_dims(kv_pool: torch.Tensor):
+    if kv_pool.dim() != 5 or kv_pool.shape[1] != 2:
+        raise ValueError("kv_pool must be [num_blocks, 2, block_size, num_kv_heads, head_dim]")
+    if not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous")
+    nb, _, bs, hkv, d = kv_pool.shape
+    return int(nb), int(bs), int(hkv), int(d)
+
+
+def _tables(block_tables: torch.Tensor, context_lens: torch.Tensor, num_seqs: int):
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous [num_seqs, max_blocks_per_seq] tensor")
+    if context_lens.shape != (num_seqs,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [num_seqs] tensor")
+    return int(block_tables.shape[1])
+
+
+def cache_write(kv_pool: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """Write each sequence's newest token (t = context_lens[s] - 1) into kv_pool in place."""
+    nb, bs, hkv, d = _pool_dims(kv_pool)
+    if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (hkv, d):
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim] matching the pool")
+    if not (key.is_contiguous() and value.is_contiguous()) or key.dtype != value.dtype:
+        raise ValueError("key/value must be contiguous and of one dtype")
+    B = int(key.shape[0])
+    mb = _tables(block_tables, context_lens, B)
+    st = load().pa_cache_write(_ptr(kv_pool), pa_dtype(kv_pool), _ptr(key), _ptr(value), pa_dtype(key),
+                               _ptr(block_tables), _ptr(context_lens), B, hkv, d, bs, mb, nb,
+                               float(k_scale), float(v_scale), _stream(stream))
+    _check(st, "pa_cache_write")
+
+
+def decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                          block_size: int, max_blocks_per_seq: int, kv_dtype: int,
+                          partition_size: int = 0) -> int:
+    n = load().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                        max_blocks_per_seq, kv_dtype, partition_size)
+    if n == 0:
+        raise RuntimeError("pa_decode_workspace_size: invalid arguments")
+    return int(n)
+
+
+def decode_partition_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                          block_size: int, max_blocks_per_seq: int, kv_dtype: int,
+                          partition_size: int = 0) -> int:
+    return int(load().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                                max_blocks_per_seq, kv_dtype, partition_size))
+
+
+class Workspace:
+    """A zero-filled device workspace for pa_decode, grown on demand.
+
+    pa_decode leaves the workspace's arrival counters at zero after every
+    completed call, so one buffer serves successive calls on one stream."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf: torch.Tensor | None = None
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tensor,
+           context_lens: torch.Tensor, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | Workspace | None = None,
+           partition_size: int = 0, stream=None) -> torch.Tensor:
+    """Paged decode attention; returns out [num_seqs, num_heads, head_dim] of query's dtype."""
+    nb, bs, hkv, d = _pool_dims(kv_pool)
+    if query.dim() != 3 or query.shape[2] != d or not query.is_contiguous():
+        raise ValueError("query must be a contiguous [num_seqs, num_heads, head_dim] tensor")
+    B, hq = int(query.shape[0]), int(query.shape[1])
+    mb = _tables(block_tables, context_lens, B)
+    if out is None:
+        out = torch.empty_like(query)
+    elif out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
+        raise ValueError("out must match query")
+    kvt = pa_dtype(kv_pool)
+    need = decode_workspace_size(B, hq, hkv, d, bs, mb, kvt, partition_size)
+    if workspace is None:
+        workspace = _default_ws.setdefault(query.device, Workspace())
+    if isinstance(workspace, Workspace):
+        ws = workspace.get(need, query.device)
+    else:
+        ws = workspace
+    st = load().pa_decode(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), kvt,
+                          _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, mb, nb,
+                          float(scale), float(k_scale), float(v_scale), int(partition_size),
+                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "pa_decode")
+    return out

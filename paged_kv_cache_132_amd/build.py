@@ -1,0 +1,58 @@
+"""Build libpa.so (the C-ABI library of HIP kernels for gfx950) in-tree.
+
+    python -m paged_kv_cache_132_amd.build
+
+compiles every source under csrc/ with hipcc for gfx950 into
+paged_kv_cache_132_amd/libpa.so.  Packed-fp32 VALU instructions are disabled
+for all device code.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+REPO = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(REPO, "include")
+LIB = os.path.join(PKG, "libpa.so")
+
+SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [
+        hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-x", "hip",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+        *[os.path.join(CSRC, s) for s in SOURCES],
+        "-o", tmp,
+    ]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build libpa.so")
+    if verbose and res.stderr.strip():
+        # the host pass does not know the packed-fp32 feature; that warning is harmless
+        lines = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
+        if lines:
+            print("\n".join(lines))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,117 @@
+// pa_cache_write kernels: put each sequence's newest K/V row into its paged
+// slot ([nano-vllm blog §4.1 step 3], [CANN notes §4.3 steps 1-3]).
+//
+// One thread moves 8 elements (16 bytes of a 16-bit source row).  Consecutive
+// threads cover consecutive 16-byte pieces of one (sequence, KV head, K|V)
+// row, so each row is one contiguous, fully coalesced segment on both sides.
+// The work is a few hundred KiB per step; the kernel is latency-bound.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWriteThreads = 256;
+constexpr int kElemsPerThread = 8;
+
+// 16-bit source element -> float32 (exact).
+template <int SRC>
+__device__ __forceinline__ float widen(uint32_t bits16) {
+    if constexpr (SRC == PA_BF16) {
+        return __uint_as_float(bits16 << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+    }
+}
+
+// float32 -> OCP e4m3 code: round to nearest, ties to even; magnitudes at or
+// beyond 448 saturate to 448; NaN keeps its sign and becomes 0x7F / 0xFF.
+__device__ __forceinline__ uint32_t e4m3_from_float(float y) {
+    const uint32_t bits = __float_as_uint(y);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (a != a) return sign | 0x7Fu;
+    if (!(a < 448.0f)) return sign | 0x7Eu;
+    if (a < 0.015625f) {
+        // Subnormal range: multiples of 2^-9.  a * 512 is exact and < 8;
+        // rintf rounds half to even.  8 (= 2^-6) becomes the smallest normal.
+        return sign | (uint32_t)rintf(a * 512.0f);
+    }
+    // Normal range [2^-6, 448): keep 3 of the 23 mantissa bits, rounding the
+    // dropped 20 bits to nearest even; a carry bumps the exponent correctly.
+    uint32_t ab = __float_as_uint(a);
+    ab += 0x7FFFFu + ((ab >> 20) & 1u);
+    const uint32_t e = (ab >> 23) - 127u + 7u;   // 1 .. 15
+    const uint32_t m = (ab >> 20) & 7u;
+    return sign | (e << 3) | m;
+}
+
+template <int SRC, int KVT>
+__global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a) {
+    const int chunks = a.head_dim / kElemsPerThread;
+    const int64_t total = (int64_t)a.num_seqs * a.num_kv_heads * 2 * chunks;
+    const int64_t i = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
+    if (i >= total) return;
+    const int c = (int)(i % chunks);
+    int64_t rest = i / chunks;
+    const int kv = (int)(rest & 1);
+    rest >>= 1;
+    const int g = (int)(rest % a.num_kv_heads);
+    const int s = (int)(rest / a.num_kv_heads);
+
+    const int L = a.context_lens[s];
+    if (L <= 0) return;
+    const int t = L - 1;
+    const int lb = t / a.block_size;
+    if (lb >= a.max_blocks_per_seq) return;
+    const int blk = a.block_tables[(int64_t)s * a.max_blocks_per_seq + lb];
+    if (blk < 0 || blk >= a.num_blocks) return;
+    const int off = t - lb * a.block_size;
+
+    const int64_t src_elem = ((int64_t)s * a.num_kv_heads + g) * a.head_dim + c * kElemsPerThread;
+    const int64_t dst_elem =
+        (((int64_t)blk * 2 + kv) * a.block_size + off) * (int64_t)a.num_kv_heads * a.head_dim +
+        (int64_t)g * a.head_dim + c * kElemsPerThread;
+    const uint4 src = *reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(kv ? a.value : a.key) + src_elem);
+
+    if constexpr (KVT != PA_FP8_E4M3) {
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kv_pool) + dst_elem) = src;
+    } else {
+        const float scale = kv ? a.v_scale : a.k_scale;
+        const uint32_t w[4] = {src.x, src.y, src.z, src.w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < kElemsPerThread; ++e) {
+            const uint32_t h = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            const float y = __fdiv_rn(widen<SRC>(h), scale);
+            packed[e >> 2] |= e4m3_from_float(y) << ((e & 3) * 8);
+        }
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.kv_pool) + dst_elem) =
+            make_uint2(packed[0], packed[1]);
+    }
+}
+
+template <int SRC, int KVT>
+int launch_typed(const WriteArgs& a, hipStream_t stream) {
+    const int64_t total = (int64_t)a.num_seqs * a.num_kv_heads * 2 * (a.head_dim / kElemsPerThread);
+    const int64_t blocks = (total + kWriteThreads - 1) / kWriteThreads;
+    hipLaunchKernelGGL((cache_write_kernel<SRC, KVT>), dim3((unsigned)blocks), dim3(kWriteThreads),
+                       0, stream, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (kv_dtype == PA_F16) return launch_typed<PA_F16, PA_F16>(a, st);
+    if (kv_dtype == PA_BF16) return launch_typed<PA_BF16, PA_BF16>(a, st);
+    if (src_dtype == PA_BF16) return launch_typed<PA_BF16, PA_FP8_E4M3>(a, st);
+    return launch_typed<PA_F16, PA_FP8_E4M3>(a, st);
+}
+
+}  // namespace pa

@@ -1,0 +1,434 @@
+// pa_decode kernel: paged decode attention in one pass with split-K and an
+// in-kernel merge ([nano-vllm blog §2.3], [CANN notes §4.3 step 4]; the
+// FlashAttention-style tiling of the computation inside a paged layout that
+// [nano-vllm blog §2.3] says composes with paging).
+//
+// Work decomposition
+//   A workgroup (4 waves) owns one (sequence, group of KV heads, partition of
+//   `partition` consecutive tokens).  One wave-wide 16-byte-per-lane load
+//   covers `rows` consecutive KV heads of ONE token: lane = (row r, slice j),
+//   `row_lanes` lanes per head row (head_dim 128 fp16: 16 lanes x 8 halves,
+//   4 heads = 1 KiB contiguous per token).  Each 16-lane/8-lane row therefore
+//   owns one KV head and keeps that head's online-softmax state on its own,
+//   with no cross-row traffic.
+//   The 4 waves take interleaved chunks of 4 tokens (chunk c -> wave c % 4),
+//   so the four waves of a workgroup stream neighbouring token rows of the
+//   same physical block together.  Each wave keeps two chunks in flight:
+//   16 x 16-byte loads per lane before it first waits.
+//
+// Per chunk (4 tokens), per lane:
+//   QK:   packed dot products (v_dot2_f32_f16 / v_dot2_f32_bf16) over the
+//         lane's 8 or 16 elements, then a 2-4 step DPP reduction inside the
+//         row; every lane of the row ends with the full score.
+//   mask: tokens at or beyond the end of the partition get weight 0 and are
+//         never loaded from their own slot (their load is redirected to the
+//         first token of the chunk, which is always valid), so poisoned or
+//         stale slots never reach the arithmetic.
+//   softmax: running max m and sum l in the exp2 domain (scores are
+//         pre-scaled by scale * log2 e), rescaling o when m grows.
+//   PV:   o[e] += p * v[e] in float32 for the lane's slice of head_dim.
+//
+// End of the workgroup: the 4 waves' states are merged through LDS.  A
+// sequence with a single partition writes its output directly.  Otherwise
+// the workgroup stores its partial (max, sum, unnormalised o), publishes it
+// with a device-scope fence and bumps the (sequence, group) arrival counter;
+// the workgroup that arrives last merges all partitions
+//     M = max_p m_p,  out = sum_p 2^(m_p-M) o_p / sum_p 2^(m_p-M) l_p
+// writes the output and resets the counter to zero for the next call.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTokensPerChunk = 4;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N = 4, 8, 16); every lane of the group
+// receives the same total.  quad_perm [1,0,3,2] and [2,3,0,1], then
+// row_half_mirror (8-lane halves) and row_mirror (16-lane rows).
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+    static_assert(N == 4 || N == 8 || N == 16, "row width");
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    if constexpr (N >= 8) x += dpp<0x141>(x);
+    if constexpr (N >= 16) x += dpp<0x140>(x);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int QT>
+__device__ __forceinline__ uint16_t to_out_bits(float x) {
+    if constexpr (QT == PA_F16) {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    } else {
+        const uint32_t b = __float_as_uint(x);
+        if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);   // NaN
+        return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+    }
+}
+
+// Dot product of a lane's K slice with a packed 16-bit query slice.
+//   16-bit KV: 4 dwords = 8 elements, q as 4 packed pairs.
+//   fp8 KV:    4 dwords = 16 codes, q as 8 packed bf16 pairs.
+template <int KVT>
+__device__ __forceinline__ float dot_slice(const uint4& k, const uint32_t* q) {
+    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+    float acc = 0.f;
+    if constexpr (KVT == PA_F16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[w]),
+                                         __builtin_bit_cast(f16x2, kw[w]), acc, false);
+    } else if constexpr (KVT == PA_BF16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[w]),
+                                                  __builtin_bit_cast(bf16x2, kw[w]), acc, false);
+    } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[w], 1.0f, false);
+            const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[w], 1.0f, true);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[2 * w]), lo, acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[2 * w + 1]), hi, acc, false);
+        }
+    }
+    return acc;
+}
+
+// o[e] += p * v[e] over a lane's V slice (8 or 16 elements).
+template <int KVT, int EPL>
+__device__ __forceinline__ void accumulate_v(float (&o)[EPL], float p, const uint4& v) {
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (KVT == PA_F16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const f16x2 h = __builtin_bit_cast(f16x2, vw[w]);
+            o[2 * w] = fmaf(p, (float)h.x, o[2 * w]);
+            o[2 * w + 1] = fmaf(p, (float)h.y, o[2 * w + 1]);
+        }
+    } else if constexpr (KVT == PA_BF16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            o[2 * w] = fmaf(p, bf16_lo(vw[w]), o[2 * w]);
+            o[2 * w + 1] = fmaf(p, bf16_hi(vw[w]), o[2 * w + 1]);
+        }
+    } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(vw[w], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(vw[w], true);
+            o[4 * w + 0] = fmaf(p, lo[0], o[4 * w + 0]);
+            o[4 * w + 1] = fmaf(p, lo[1], o[4 * w + 1]);
+            o[4 * w + 2] = fmaf(p, hi[0], o[4 * w + 2]);
+            o[4 * w + 3] = fmaf(p, hi[1], o[4 * w + 3]);
+        }
+    }
+}
+
+template <int QT, int KVT, int D, int G>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
+    constexpr int KVB = KVT == PA_FP8_E4M3 ? 1 : 2;
+    constexpr int ROWL = D * KVB / 16;      // lanes per KV-head row
+    constexpr int ROWS = 64 / ROWL;         // KV heads per workgroup
+    constexpr int EPL = 16 / KVB;           // KV elements per lane per token
+    constexpr int QDW = EPL / 2;            // packed 16-bit query pairs per lane
+    constexpr int NW = kDecodeWaves;
+    constexpr int TPC = kTokensPerChunk;
+    constexpr int OPT = EPL / NW;           // output elements per thread in the merge
+
+    __shared__ float s_m[NW][ROWS];
+    __shared__ float s_l[NW][ROWS];
+    __shared__ float s_o[NW][64 * EPL];
+    __shared__ int s_last;
+
+    // ---- which (sequence, KV-head group, partition) -------------------------
+    const int wg = blockIdx.x;
+    const int group = wg % a.groups;
+    const int rest = wg / a.groups;
+    const int s = rest % a.num_seqs;
+    const int p = rest / a.num_seqs;
+
+    const int max_tokens = a.max_blocks_per_seq << a.block_shift;
+    const int L = min(a.context_lens[s], max_tokens);
+    const int n_part = L > 0 ? (L + a.partition - 1) / a.partition : 0;
+    if (p >= (n_part > 0 ? n_part : 1)) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane / ROWL;
+    const int j = lane % ROWL;
+    const int g_row = group * ROWS + r;
+    const bool row_ok = g_row < a.num_kv_heads;
+    const int g = row_ok ? g_row : a.num_kv_heads - 1;   // rows past the last head idle on a valid one
+    const int Hq = a.num_heads;
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+
+    if (L <= 0) {                                          // empty sequence: zero output
+        if (wave == 0 && row_ok) {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                uint16_t* dst = out + ((int64_t)s * Hq + g * G + gi) * D + j * EPL;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) dst[e] = 0;
+            }
+        }
+        return;
+    }
+
+    // ---- query slices of the G query heads that read KV head g ------------
+    uint32_t q[G][QDW];
+    {
+        const uint16_t* qb = static_cast<const uint16_t*>(a.query) + ((int64_t)s * Hq + g * G) * D + j * EPL;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+            for (int w = 0; w < QDW; w += 4) {
+                const uint4 v = *reinterpret_cast<const uint4*>(qb + gi * D + 2 * w);
+                q[gi][w] = v.x; q[gi][w + 1] = v.y; q[gi][w + 2] = v.z; q[gi][w + 3] = v.w;
+            }
+        }
+    }
+
+    // ---- the partition's token range and this lane's K/V addressing -------
+    const int t_begin = p * a.partition;
+    const int t_end = min(L, t_begin + a.partition);
+    const int n_chunks = (t_end - t_begin + TPC - 1) / TPC;
+    const int64_t row_stride = (int64_t)a.num_kv_heads * D;              // elements per token row
+    const int64_t half_stride = row_stride << a.block_shift;             // K half -> V half
+    const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
+    const int64_t lane_off = ((int64_t)g * D + j * EPL) * KVB;           // bytes within a token row
+    const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+    float m[G], l[G], o[G][EPL];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        m[gi] = -INFINITY;
+        l[gi] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[gi][e] = 0.f;
+    }
+
+    // Issue the 4 K rows and 4 V rows of chunk c into kr / vr.  Returns the
+    // number of valid tokens (0 when the block id is outside the pool).
+    auto load_chunk = [&](int c, uint4 (&kr)[TPC], uint4 (&vr)[TPC]) -> int {
+        const int tc = t_begin + c * TPC;
+        const int blk = bt_row[tc >> a.block_shift];
+        const int nvalid = (blk >= 0 && blk < a.num_blocks) ? min(TPC, t_end - tc) : 0;
+        const int blk_safe = nvalid ? blk : 0;
+        const int off = tc & (a.block_size - 1);
+        const uint8_t* kbase =
+            pool + (((int64_t)blk_safe * 2 << a.block_shift) + off) * row_stride * KVB + lane_off;
+#pragma unroll
+        for (int i = 0; i < TPC; ++i) {
+            const int ii = i < nvalid ? i : 0;
+            kr[i] = *reinterpret_cast<const uint4*>(kbase + ii * row_stride * KVB);
+        }
+#pragma unroll
+        for (int i = 0; i < TPC; ++i) {
+            const int ii = i < nvalid ? i : 0;
+            vr[i] = *reinterpret_cast<const uint4*>(kbase + (half_stride + ii * row_stride) * KVB);
+        }
+        return nvalid;
+    };
+
+    auto compute_chunk = [&](int nvalid, const uint4 (&kr)[TPC], const uint4 (&vr)[TPC]) {
+        if (nvalid <= 0) return;
+        float sc[TPC][G];
+#pragma unroll
+        for (int i = 0; i < TPC; ++i) {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+                sc[i][gi] = row_sum<ROWL>(dot_slice<KVT>(kr[i], q[gi])) * a.score_scale;
+        }
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            float mx = sc[0][gi];
+#pragma unroll
+            for (int i = 1; i < TPC; ++i) mx = i < nvalid ? fmaxf(mx, sc[i][gi]) : mx;
+            const float m_new = fmaxf(m[gi], mx);
+            const float alpha = fast_exp2(m[gi] - m_new);   // m_new is finite: token 0 is valid
+            float pr[TPC];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < TPC; ++i) {
+                pr[i] = i < nvalid ? fast_exp2(sc[i][gi] - m_new) : 0.f;
+                psum += pr[i];
+            }
+            l[gi] = l[gi] * alpha + psum;
+            m[gi] = m_new;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[gi][e] *= alpha;
+#pragma unroll
+            for (int i = 0; i < TPC; ++i) accumulate_v<KVT, EPL>(o[gi], pr[i], vr[i]);
+        }
+    };
+
+    // ---- main loop: two chunks in flight per wave --------------------------
+    {
+        uint4 ka[TPC], va[TPC], kb[TPC], vb[TPC];
+        int c = wave;
+        if (c < n_chunks) {
+            int na = load_chunk(c, ka, va);
+            while (true) {
+                int nb = 0;
+                if (c + NW < n_chunks) nb = load_chunk(c + NW, kb, vb);
+                compute_chunk(na, ka, va);
+                c += NW;
+                if (c >= n_chunks) break;
+                if (c + NW < n_chunks) na = load_chunk(c + NW, ka, va);
+                compute_chunk(nb, kb, vb);
+                c += NW;
+                if (c >= n_chunks) break;
+            }
+        }
+    }
+
+    // ---- merge the 4 waves, then finish or publish a partial ---------------
+    const int ln = tid & 63;          // lane slot this thread merges
+    const int part = tid >> 6;        // which quarter of that slot's elements
+    const int mr = ln / ROWL;
+    const int mj = ln % ROWL;
+    const int mg_row = group * ROWS + mr;
+    const bool m_ok = mg_row < a.num_kv_heads;
+    const int P = a.max_partitions;
+
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        if (j == 0) {
+            s_m[wave][r] = m[gi];
+            s_l[wave][r] = l[gi];
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_o[wave][lane * EPL + e] = o[gi][e];
+        __syncthreads();
+
+        float M = s_m[0][mr];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][mr]);
+        float fw[NW];
+        float Lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            fw[w] = fast_exp2(s_m[w][mr] - M);            // idle waves: 2^-inf = 0
+            Lsum += fw[w] * s_l[w][mr];
+        }
+        float acc[OPT];
+#pragma unroll
+        for (int e = 0; e < OPT; ++e) {
+            float x = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) x = fmaf(fw[w], s_o[w][ln * EPL + part * OPT + e], x);
+            acc[e] = x;
+        }
+        const int h = mg_row * G + gi;
+        const int d0 = mj * EPL + part * OPT;
+        if (m_ok) {
+            if (n_part == 1) {
+                const float inv = a.v_scale / Lsum;
+                uint16_t* dst = out + ((int64_t)s * Hq + h) * D + d0;
+#pragma unroll
+                for (int e = 0; e < OPT; ++e) dst[e] = to_out_bits<QT>(acc[e] * inv);
+            } else {
+                const int64_t slot = ((int64_t)s * Hq + h) * P + p;
+                float* po = a.part_o + slot * D + d0;
+#pragma unroll
+                for (int e = 0; e < OPT; ++e) po[e] = acc[e];
+                if (mj == 0 && part == 0) {
+                    a.part_ml[slot * 2] = M;
+                    a.part_ml[slot * 2 + 1] = Lsum;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (n_part == 1) return;
+
+    // ---- split-K: the last partition to arrive merges ----------------------
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const int old = atomicAdd(&a.counters[s * a.groups + group], 1);
+        s_last = (old == n_part - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    if (m_ok) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            const int h = mg_row * G + gi;
+            const int64_t base = ((int64_t)s * Hq + h) * P;
+            float M = -INFINITY;
+            for (int pp = 0; pp < n_part; ++pp) M = fmaxf(M, a.part_ml[(base + pp) * 2]);
+            float den = 0.f;
+            float num[OPT];
+#pragma unroll
+            for (int e = 0; e < OPT; ++e) num[e] = 0.f;
+            const int d0 = mj * EPL + part * OPT;
+            for (int pp = 0; pp < n_part; ++pp) {
+                const float f = fast_exp2(a.part_ml[(base + pp) * 2] - M);
+                den = fmaf(f, a.part_ml[(base + pp) * 2 + 1], den);
+                const float* po = a.part_o + (base + pp) * D + d0;
+#pragma unroll
+                for (int e = 0; e < OPT; ++e) num[e] = fmaf(f, po[e], num[e]);
+            }
+            const float inv = a.v_scale / den;
+            uint16_t* dst = out + ((int64_t)s * Hq + h) * D + d0;
+#pragma unroll
+            for (int e = 0; e < OPT; ++e) dst[e] = to_out_bits<QT>(num[e] * inv);
+        }
+    }
+    if (tid == 0) atomicExch(&a.counters[s * a.groups + group], 0);
+}
+
+template <int QT, int KVT, int D>
+int launch_d(const DecodeArgs& a, const DecodePlan& plan, int group_size, hipStream_t st) {
+    const dim3 grid((unsigned)plan.grid), block(kDecodeThreads);
+    switch (group_size) {
+        case 1: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 1>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 2>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 4>), grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 8>), grid, block, 0, st, a); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+template <int QT, int KVT>
+int launch_t(const DecodeArgs& a, const DecodePlan& plan, int head_dim, int group_size, hipStream_t st) {
+    if (head_dim == 64) return launch_d<QT, KVT, 64>(a, plan, group_size, st);
+    return launch_d<QT, KVT, 128>(a, plan, group_size, st);
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype, pa_dtype kv_dtype,
+                  int head_dim, int group_size, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (plan.grid == 0) return 0;
+    if (kv_dtype == PA_F16) return launch_t<PA_F16, PA_F16>(a, plan, head_dim, group_size, st);
+    if (kv_dtype == PA_BF16) return launch_t<PA_BF16, PA_BF16>(a, plan, head_dim, group_size, st);
+    return launch_t<PA_BF16, PA_FP8_E4M3>(a, plan, head_dim, group_size, st);
+}
+
+}  // namespace pa

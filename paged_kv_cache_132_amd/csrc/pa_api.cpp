@@ -1,0 +1,245 @@
+// Host side of the C ABI: argument checks, the split-K launch plan, workspace
+// layout and kernel launches.  No device memory is allocated here and no call
+// waits for the device.
+#include <hip/hip_runtime_api.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+bool known_dtype(pa_dtype d) { return d == PA_F16 || d == PA_BF16 || d == PA_FP8_E4M3; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_exact(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return (1 << s) == x ? s : -1;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kMaxPartition = 1 << 20;
+
+}  // namespace
+
+DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype) {
+    DecodeGeometry g;
+    g.kv_bytes = kv_dtype == PA_FP8_E4M3 ? 1 : 2;
+    g.row_lanes = head_dim * g.kv_bytes / 16;
+    g.rows = 64 / g.row_lanes;
+    g.elems = 16 / g.kv_bytes;
+    return g;
+}
+
+pa_status check_decode_args(const void* out, const void* query, pa_dtype q_dtype,
+                            const void* kv_pool, pa_dtype kv_dtype,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                            int32_t num_blocks, float scale, float k_scale, float v_scale,
+                            int32_t partition_size) {
+    if (!known_dtype(q_dtype) || !known_dtype(kv_dtype)) return PA_ERR_BAD_DTYPE;
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || partition_size < 0)
+        return PA_ERR_BAD_SHAPE;
+    if (num_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+    const int group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    const bool combo = (q_dtype == PA_F16 && kv_dtype == PA_F16) ||
+                       (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
+                       (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3);
+    if (!combo) return PA_ERR_UNSUPPORTED;
+    if (partition_size != 0 && (partition_size % block_size != 0 || partition_size > kMaxPartition))
+        return PA_ERR_BAD_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)INT32_MAX / 2) return PA_ERR_BAD_SHAPE;
+    if (!isfinite(scale)) return PA_ERR_BAD_SHAPE;
+    if (kv_dtype == PA_FP8_E4M3 &&
+        !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+        return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !query || !kv_pool || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(kv_pool) || !aligned16(block_tables) ||
+        !aligned16(context_lens))
+        return PA_ERR_MISALIGNED;
+    return PA_OK;
+}
+
+bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t block_size, int32_t max_blocks_per_seq, pa_dtype kv_dtype,
+                 int32_t partition_size, DecodePlan* plan) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        block_size <= 0 || partition_size < 0 || num_heads % num_kv_heads != 0)
+        return false;
+    if (head_dim != 64 && head_dim != 128) return false;
+    if (!known_dtype(kv_dtype)) return false;
+    if (partition_size != 0 && (partition_size % block_size != 0 || partition_size > kMaxPartition))
+        return false;
+    DecodePlan p;
+    p.geo = decode_geometry(head_dim, kv_dtype);
+    p.groups = (num_kv_heads + p.geo.rows - 1) / p.geo.rows;
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+    int part = partition_size;
+    if (part == 0) {
+        // Enough workgroups to fill 256 CUs several times over when every
+        // sequence is at its longest, without splitting sequences into
+        // slivers whose partial results cost more than they save.
+        const int64_t heads_x_seqs = (int64_t)p.groups * num_seqs;
+        part = 512;
+        while (part > 64 && heads_x_seqs * ((max_tokens + part - 1) / part) < 2048) part /= 2;
+        if (part < block_size) part = block_size;
+        part = (part + block_size - 1) / block_size * block_size;
+    }
+    p.partition = part;
+    p.max_partitions = (int)((max_tokens + part - 1) / part);
+    p.grid = (int64_t)p.groups * num_seqs * p.max_partitions;
+    if (p.grid > INT32_MAX) return false;
+    const size_t n_cnt = (size_t)num_seqs * p.groups;
+    const size_t n_part = (size_t)num_seqs * num_heads * p.max_partitions;
+    p.off_counters = 0;
+    p.off_ml = align_up(n_cnt * sizeof(int32_t), 256);
+    p.off_o = p.off_ml + align_up(n_part * 2 * sizeof(float), 256);
+    p.bytes = p.off_o + align_up(n_part * (size_t)head_dim * sizeof(float), 256);
+    if (p.bytes == 0) p.bytes = 256;
+    *plan = p;
+    return true;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_NULL_POINTER: return "PA_ERR_NULL_POINTER";
+        case PA_ERR_BAD_SHAPE: return "PA_ERR_BAD_SHAPE";
+        case PA_ERR_BAD_DTYPE: return "PA_ERR_BAD_DTYPE";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_MISALIGNED: return "PA_ERR_MISALIGNED";
+        case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+    }
+    return "PA_ERR_UNKNOWN";
+}
+
+pa_status pa_cache_write(void* kv_pool, pa_dtype kv_dtype, const void* key, const void* value,
+                         pa_dtype src_dtype, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int32_t num_blocks, float k_scale, float v_scale, void* stream) {
+    if (!known_dtype(kv_dtype) || !known_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
+    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return PA_ERR_BAD_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    const bool combo = (src_dtype == kv_dtype && src_dtype != PA_FP8_E4M3) ||
+                       (kv_dtype == PA_FP8_E4M3 && (src_dtype == PA_BF16 || src_dtype == PA_F16));
+    if (!combo) return PA_ERR_UNSUPPORTED;
+    if (kv_dtype == PA_FP8_E4M3 &&
+        !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+        return PA_ERR_BAD_SHAPE;
+    if ((int64_t)num_seqs * num_kv_heads * head_dim * 2 > (int64_t)INT32_MAX) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!kv_pool || !key || !value || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
+    if (!aligned16(kv_pool) || !aligned16(key) || !aligned16(value) || !aligned16(block_tables) ||
+        !aligned16(context_lens))
+        return PA_ERR_MISALIGNED;
+
+    WriteArgs a;
+    a.kv_pool = kv_pool;
+    a.key = key;
+    a.value = value;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return launch_cache_write(a, src_dtype, kv_dtype, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                 pa_dtype kv_dtype, int32_t requested) {
+    DecodePlan p;
+    if (!plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     kv_dtype, requested, &p))
+        return 0;
+    return p.partition;
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                pa_dtype kv_dtype, int32_t partition_size) {
+    DecodePlan p;
+    if (!plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     kv_dtype, partition_size, &p))
+        return 0;
+    return p.bytes;
+}
+
+pa_status pa_decode(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
+                    pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                    float scale, float k_scale, float v_scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    pa_status st = check_decode_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables,
+                                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                     block_size, max_blocks_per_seq, num_blocks, scale, k_scale,
+                                     v_scale, partition_size);
+    if (st != PA_OK) return st;
+    if (num_seqs == 0) return PA_OK;
+    DecodePlan plan;
+    if (!plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     kv_dtype, partition_size, &plan))
+        return PA_ERR_BAD_SHAPE;
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
+    if (workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+
+    const bool fp8 = kv_dtype == PA_FP8_E4M3;
+    DecodeArgs a;
+    a.out = out;
+    a.query = query;
+    a.kv_pool = kv_pool;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<int32_t*>(ws + plan.off_counters);
+    a.part_ml = reinterpret_cast<float*>(ws + plan.off_ml);
+    a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.block_shift = log2_exact(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.groups = plan.groups;
+    a.partition = plan.partition;
+    a.max_partitions = plan.max_partitions;
+    a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
+    a.v_scale = fp8 ? v_scale : 1.0f;
+    const int err = launch_decode(a, plan, q_dtype, kv_dtype, head_dim, num_heads / num_kv_heads,
+                                  stream);
+    return err == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal interfaces of the paged-attention library: launch plans, kernel
+// argument blocks and launcher entry points shared by the host API and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Threads per workgroup of the decode kernel: four wave64 waves.
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = kDecodeThreads / 64;
+
+// Geometry of the decode kernel for one (head_dim, kv dtype): a K or V row of
+// one KV head (head_dim elements) is read by `row_lanes` lanes with one
+// 16-byte load each, so one wave-wide load covers `rows` = 64 / row_lanes
+// consecutive KV heads of one token.  A workgroup owns such a group of heads.
+struct DecodeGeometry {
+    int kv_bytes;    // bytes per KV element
+    int row_lanes;   // lanes per KV-head row
+    int rows;        // KV heads per workgroup
+    int elems;       // KV elements per lane per token (16 / kv_bytes)
+};
+
+DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype);
+
+// Host-side launch plan of one pa_decode call.
+struct DecodePlan {
+    DecodeGeometry geo;
+    int groups;          // ceil(num_kv_heads / rows)
+    int partition;       // tokens per split-K partition (multiple of block_size)
+    int max_partitions;  // ceil(max_blocks_per_seq * block_size / partition)
+    int64_t grid;        // workgroups launched
+    size_t off_counters, off_ml, off_o, bytes;   // workspace layout
+};
+
+// Pure argument checks (no HIP calls): shared by the API and the CPU tests.
+pa_status check_decode_args(const void* out, const void* query, pa_dtype q_dtype,
+                            const void* kv_pool, pa_dtype kv_dtype,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                            int32_t num_blocks, float scale, float k_scale, float v_scale,
+                            int32_t partition_size);
+bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t block_size, int32_t max_blocks_per_seq, pa_dtype kv_dtype,
+                 int32_t partition_size, DecodePlan* plan);
+
+struct DecodeArgs {
+    void* out;
+    const void* query;
+    const void* kv_pool;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int32_t* counters;      // [num_seqs * groups]
+    float* part_ml;         // [num_seqs, num_heads, max_partitions, 2] (max, sum) log2 domain
+    float* part_o;          // [num_seqs, num_heads, max_partitions, head_dim]
+    int32_t num_seqs, num_heads, num_kv_heads;
+    int32_t block_size, block_shift, max_blocks_per_seq, num_blocks;
+    int32_t groups, partition, max_partitions;
+    float score_scale;      // scale * k_scale * log2(e): scores in the exp2 domain
+    float v_scale;
+};
+
+struct WriteArgs {
+    void* kv_pool;
+    const void* key;
+    const void* value;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int32_t num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks;
+    float k_scale, v_scale;
+};
+
+// Launchers (defined next to their kernels).  Return the hipError_t as int.
+int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype, pa_dtype kv_dtype,
+                  int head_dim, int group_size, void* stream);
+int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream);
+
+}  // namespace pa

@@ -1,0 +1,94 @@
+"""Helpers shared by the GPU parity tests: device upload, poisoning, comparison.
+
+The GPU side is reached only through the C ABI (via the ctypes binding);
+expected values come only from the CPU oracle.
+"""
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_132_amd as pa
+
+TORCH16 = {"f16": torch.float16, "bf16": torch.bfloat16}
+POISON = {"f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F}   # a NaN in each format
+
+# Max-abs tolerances on decode outputs: 2e-3 for 16-bit KV, 2e-2 for fp8 KV
+# (against the oracle on dequantised values).  A bf16 output additionally
+# carries its own rounding, at most 2^-8 relative to the value.
+TOL = {"f16": 2e-3, "bf16": 2e-3, "fp8_e4m3": 2e-2}
+
+
+def dev16(raw: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(TORCH16[dtype]).cuda()
+
+
+def dev_pool(pool_raw: np.ndarray, kv_dtype: str) -> torch.Tensor:
+    if kv_dtype == "fp8_e4m3":
+        return torch.from_numpy(np.ascontiguousarray(pool_raw).view(np.uint8)).cuda()
+    return dev16(pool_raw, kv_dtype)
+
+
+def dev_i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.uint8:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def used_slots_mask(tables, lens, num_blocks: int, bs: int) -> np.ndarray:
+    """[num_blocks, bs] bool: which (block, offset) slots some sequence reads."""
+    used = np.zeros((num_blocks, bs), dtype=bool)
+    for tab, L in zip(tables, lens):
+        L = int(L)
+        if L <= 0:
+            continue
+        n = -(-L // bs)
+        used[np.asarray(tab[: n - 1], dtype=np.int64)] = True
+        used[tab[n - 1], : L - (n - 1) * bs] = True
+    return used
+
+
+def poison_unused(pool_raw: np.ndarray, tables, lens, kv_dtype: str) -> np.ndarray:
+    """Copy of the pool with every slot no sequence reads set to NaN."""
+    nb, _, bs = pool_raw.shape[:3]
+    used = used_slots_mask(tables, lens, nb, bs)
+    out = pool_raw.copy()
+    blocks, offs = np.nonzero(~used)
+    out[blocks, :, offs] = POISON[kv_dtype]
+    return out
+
+
+def pool_of(batch) -> np.ndarray:
+    """Raw pool the decode reads: 16-bit bits, or oracle-encoded e4m3 codes."""
+    if batch.kv_dtype == "fp8_e4m3":
+        return oracle.encode_pool(batch.kv_source, batch.src_dtype, "fp8_e4m3", batch.k_scale, batch.v_scale)
+    return batch.kv_pool
+
+
+def gpu_decode(batch, pool_dev, query_raw, bt, lens, partition_size=0, workspace=None):
+    q = dev16(query_raw, batch.q_dtype)
+    out = pa.decode(q, pool_dev, dev_i32(bt), dev_i32(lens), batch.scale, batch.k_scale, batch.v_scale,
+                    workspace=workspace, partition_size=partition_size)
+    torch.cuda.synchronize()
+    return oracle.to_f64(host_bits(out), batch.q_dtype)
+
+
+def oracle_decode(batch, pool_raw, query_raw, bt, lens, seqs=None):
+    return oracle.paged_decode(query_raw, batch.q_dtype, pool_raw, batch.kv_dtype, bt, lens,
+                               batch.block_size, batch.scale, batch.k_scale, batch.v_scale, seqs=seqs)
+
+
+def assert_decode_close(got, ref, batch, seqs=None):
+    if seqs is not None:
+        got, ref = got[list(seqs)], ref[list(seqs)]
+    assert np.isfinite(got).all(), "non-finite output"
+    tol = TOL[batch.kv_dtype]
+    bound = tol + (np.abs(ref) * 2.0 ** -8 if batch.q_dtype == "bf16" else 0.0)
+    err = np.abs(got - ref)
+    worst = float((err - bound).max()) if err.size else 0.0
+    assert worst <= 0, f"max abs err {err.max():.3e} (tolerance {tol:g})"
+    return float(err.max()) if err.size else 0.0

@@ -1,0 +1,237 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Cache writes must match bit for bit over the whole pool; decode outputs must
+match within max-abs 2e-3 (16-bit KV) or 2e-2 (fp8 KV).  Slots no sequence
+reads are poisoned with NaN, so any stray read shows up as a non-finite
+output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_132_amd as pa
+from tests._gpu import (
+    POISON, assert_decode_close, dev16, dev_i32, dev_pool, gpu_decode, host_bits, oracle_decode,
+    poison_unused, pool_of,
+)
+from workloads import make_custom, make_prefix_shared, make_tiny, make_mixed, make_llama7b
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_case(batch, partition_sizes=(0,)):
+    bt = batch.block_table_array()
+    lens = batch.context_lens
+    pool = poison_unused(pool_of(batch), batch.tables, lens, batch.kv_dtype)
+    pool_dev = dev_pool(pool, batch.kv_dtype)
+    ref = oracle_decode(batch, pool, batch.query, bt, lens)
+    for ps in partition_sizes:
+        got = gpu_decode(batch, pool_dev, batch.query, bt, lens, partition_size=ps)
+        assert_decode_close(got, ref, batch)
+
+
+# ---------------------------------------------------------------------------
+# the tiny workload: decode, write one token per sequence, decode again
+
+def test_tiny_decode_write_decode():
+    b = make_tiny()
+    bt0, lens0 = b.block_table_array(), b.context_lens.copy()
+    pool = poison_unused(b.kv_pool, b.tables, lens0, "f16")
+    pool_dev = dev_pool(pool, "f16")
+    assert_decode_close(gpu_decode(b, pool_dev, b.query, bt0, lens0),
+                        oracle_decode(b, pool, b.query, bt0, lens0), b)
+
+    lens1 = lens0 + 1
+    for tab, L in zip(b.tables, lens1):
+        b.manager.grow_to(tab, int(L))
+    bt1 = b.block_table_array()
+    pa.cache_write(pool_dev, dev16(b.new_key[0], "f16"), dev16(b.new_value[0], "f16"),
+                   dev_i32(bt1), dev_i32(lens1))
+    torch.cuda.synchronize()
+    pool1 = oracle.cache_write(pool, "f16", b.new_key[0], b.new_value[0], "f16", bt1, lens1, 16)
+    assert np.array_equal(host_bits(pool_dev), pool1)
+
+    assert_decode_close(gpu_decode(b, pool_dev, b.step_query[0], bt1, lens1),
+                        oracle_decode(b, pool1, b.step_query[0], bt1, lens1), b)
+
+
+# ---------------------------------------------------------------------------
+# scaled-down shapes of every workload, split into several partitions
+
+SMALL_CASES = {
+    # name: (lens, Hq, Hkv, D, bs, q_dtype, kv_dtype)
+    "mha_f16_d128_bs16": ([1, 15, 16, 17, 129, 300], 32, 32, 128, 16, "f16", "f16"),
+    "mha_f16_d128_bs32": ([5, 33, 64, 100, 257], 32, 32, 128, 32, "f16", "f16"),
+    "mha_f16_d64_bs16": ([20, 37, 16, 1, 200], 8, 8, 64, 16, "f16", "f16"),
+    "mha_bf16_d128_bs16": ([3, 50, 77, 400], 16, 16, 128, 16, "bf16", "bf16"),
+    "mha_bf16_d64_bs32": ([3, 50, 77, 130], 8, 8, 64, 32, "bf16", "bf16"),
+    "gqa2_f16_d128": ([9, 64, 300], 16, 8, 128, 16, "f16", "f16"),
+    "gqa4_f16_d64": ([9, 64, 300], 32, 8, 64, 32, "f16", "f16"),
+    "gqa8_bf16_d64_partial_group": ([7, 90, 33], 16, 2, 64, 16, "bf16", "bf16"),
+    "mqa_f16_d128": ([1, 31, 250], 8, 1, 128, 16, "f16", "f16"),
+    "gqa4_fp8_d128_bs16": ([16, 100, 333, 1, 64, 700], 32, 8, 128, 16, "bf16", "fp8_e4m3"),
+    "gqa4_fp8_d128_bs32": ([16, 100, 333, 1], 32, 8, 128, 32, "bf16", "fp8_e4m3"),
+    "gqa2_fp8_d64": ([40, 120, 2], 8, 4, 64, 16, "bf16", "fp8_e4m3"),
+    "mha_fp8_d128_partial_group": ([40, 160], 4, 4, 128, 16, "bf16", "fp8_e4m3"),
+    "gqa8_fp8_d128": ([40, 160], 16, 2, 128, 16, "bf16", "fp8_e4m3"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+def test_small_case(name):
+    lens, hq, hkv, d, bs, qd, kvd = SMALL_CASES[name]
+    b = make_custom(name, 100 + sorted(SMALL_CASES).index(name), lens, hq, hkv, d, bs, qd, kvd)
+    _run_case(b, partition_sizes=(0, bs, 2 * bs, 64 if bs == 16 else 96, b.max_blocks_per_seq * bs))
+
+
+def test_zero_and_one_token_sequences():
+    b = make_custom("edge", 7, [0, 1, 18, 0, 1], 8, 8, 128, 16, "f16", "f16")
+    bt, lens = b.block_table_array(pad=0), b.context_lens
+    pool = b.kv_pool
+    got = gpu_decode(b, dev_pool(pool, "f16"), b.query, bt, lens, partition_size=16)
+    assert np.all(got[0] == 0) and np.all(got[3] == 0)
+    for s in (1, 4):                           # one token: the output is that token's V, exactly
+        v = oracle.to_f64(pool[b.tables[s][0], 1, 0], "f16")
+        assert np.array_equal(got[s], v)
+    assert_decode_close(got, oracle_decode(b, pool, b.query, bt, lens), b)
+
+
+# ---------------------------------------------------------------------------
+# addressing: one-hot probe and physical-block permutation
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_one_hot_probe_reads_the_addressed_slot(bs):
+    """q = 16 e_0 and only the probe token has K[.,0] = 40: its weight exceeds
+    every other by e^50, so the output is that token's V row bit for bit."""
+    lens = [3 * bs + 5, 2 * bs, 9 * bs + 1, 1]
+    b = make_custom(f"probe{bs}", 8, lens, 8, 8, 128, bs, "f16", "f16")
+    bt = b.block_table_array()
+    q = np.zeros_like(b.query.view(np.float16))
+    q[:, :, 0] = 16.0
+    q = q.view(np.uint16)
+    pool0 = b.kv_pool.view(np.float16).copy()
+    pool0[:, 0, :, :, 0] = 0.0
+    for t_rel in (0, bs - 1, bs, -1):
+        pool = pool0.copy()
+        targets = []
+        for s, L in enumerate(lens):
+            t = t_rel % L
+            blk, off = b.tables[s][t // bs], t % bs
+            pool[blk, 0, off, :, 0] = 40.0
+            targets.append((blk, off))
+        pool_u = pool.view(np.uint16)
+        got = gpu_decode(b, dev_pool(pool_u, "f16"), q, bt, b.context_lens, partition_size=bs)
+        for s, (blk, off) in enumerate(targets):
+            assert np.array_equal(got[s], oracle.to_f64(pool_u[blk, 1, off], "f16")), (s, t_rel)
+
+
+def test_permuting_physical_blocks_is_bit_identical():
+    b = make_custom("perm", 9, [37, 16, 700, 3, 129], 32, 32, 128, 16, "f16", "f16")
+    bt = b.block_table_array()
+    pool = b.kv_pool
+    ref = gpu_decode(b, dev_pool(pool, "f16"), b.query, bt, b.context_lens, partition_size=64)
+    perm = np.random.default_rng(10).permutation(b.num_blocks)
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
+    got = gpu_decode(b, dev_pool(pool2, "f16"), b.query, bt2, b.context_lens, partition_size=64)
+    assert np.array_equal(got, ref)
+
+
+def test_workspace_is_reusable_and_counters_return_to_zero():
+    b = make_custom("ws", 11, [300, 600, 5], 16, 16, 128, 16, "f16", "f16")
+    bt, lens = dev_i32(b.block_table_array()), dev_i32(b.context_lens)
+    pool = dev_pool(b.kv_pool, "f16")
+    q = dev16(b.query, "f16")
+    need = pa.decode_workspace_size(3, 16, 16, 128, 16, b.max_blocks_per_seq, pa.PA_F16, 64)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = [pa.decode(q, pool, bt, lens, b.scale, workspace=ws, partition_size=64) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    groups = 16 // 4
+    assert int(ws[: 3 * groups * 4].view(torch.int32).abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# fp8 cache write: bit-exact quantisation, special values included
+
+def test_fp8_write_bit_exact_with_special_values():
+    B, Hkv, D, bs = 6, 8, 128, 16
+    b = make_custom("fp8w", 12, [1, 16, 17, 40, 5, 33], 32, Hkv, D, bs, "bf16", "fp8_e4m3")
+    bt, lens = b.block_table_array(), b.context_lens
+    rng = np.random.default_rng(13)
+    grid = oracle.e4m3_decode_table()[:0x7F]
+    mids = ((grid[1:] + grid[:-1]) / 2)
+    special = np.concatenate([mids, -mids, grid, -grid, [448, 464, 465, 480, 1e4, -1e4, 2.0 ** -10,
+                                                        2.0 ** -11, 3 * 2.0 ** -11, 1e-30, -0.0, 0.0,
+                                                        np.inf, -np.inf, np.nan]])
+    vals = rng.standard_normal((2, B, Hkv, D)).astype(np.float32) * 30
+    flat = vals.reshape(-1)
+    flat[: special.size] = special.astype(np.float32)
+    from workloads.configs import _f32_to_bf16_bits   # input generation only
+    # bf16 holds every e4m3 value and midpoint exactly; special values stay special
+    src = _f32_to_bf16_bits(np.nan_to_num(vals, nan=0.0, posinf=0.0, neginf=0.0))
+    src = src.reshape(2, B, Hkv, D)
+    sflat = src.reshape(-1)
+    sflat[: special.size] = (special.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    pool = np.full(b.kv_source.shape, POISON["fp8_e4m3"], dtype=np.uint8)
+    for k_scale, v_scale in ((1.0, 1.0), (b.k_scale, b.v_scale), (0.37, 3.0)):
+        pool_dev = dev_pool(pool, "fp8_e4m3")
+        pa.cache_write(pool_dev, dev16(src[0], "bf16"), dev16(src[1], "bf16"), dev_i32(bt), dev_i32(lens),
+                       k_scale, v_scale)
+        torch.cuda.synchronize()
+        ref = oracle.cache_write(pool, "fp8_e4m3", src[0], src[1], "bf16", bt, lens, bs, k_scale, v_scale)
+        got = host_bits(pool_dev).reshape(ref.shape)
+        assert np.array_equal(got, ref), (k_scale, v_scale, int((got != ref).sum()))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_16bit_write_bit_exact(dtype):
+    b = make_custom("w16", 14, [1, 16, 17, 40, 5, 33, 64], 16, 16, 128, 32, dtype, dtype)
+    bt, lens = b.block_table_array(), b.context_lens
+    pool = poison_unused(b.kv_pool, b.tables, lens - 1, dtype)
+    pool_dev = dev_pool(pool, dtype)
+    pa.cache_write(pool_dev, dev16(b.new_key[0], dtype), dev16(b.new_value[0], dtype), dev_i32(bt), dev_i32(lens))
+    torch.cuda.synchronize()
+    ref = oracle.cache_write(pool, dtype, b.new_key[0], b.new_value[0], dtype, bt, lens, 32)
+    assert np.array_equal(host_bits(pool_dev).reshape(ref.shape), ref)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+
+def test_mixed_append_steps():
+    """The mixed-length batch, 33 steps of append-one-token then decode, at
+    block sizes 16 and 32; new blocks come from the host allocator exactly
+    when a tail block fills ([CANN notes §4.3])."""
+    for bs in (16, 32):
+        b = make_mixed(block_size=bs, steps=33)
+        lens = b.context_lens.copy()
+        bt = b.block_table_array()
+        pool = poison_unused(b.kv_pool, b.tables, lens, "f16")
+        pool_dev = dev_pool(pool, "f16")
+        for step in range(33):
+            lens = lens + 1
+            for tab, L in zip(b.tables, lens):
+                b.manager.grow_to(tab, int(L))
+            bt = b.block_table_array()
+            pa.cache_write(pool_dev, dev16(b.new_key[step], "f16"), dev16(b.new_value[step], "f16"),
+                           dev_i32(bt), dev_i32(lens))
+            pool = oracle.cache_write(pool, "f16", b.new_key[step], b.new_value[step], "f16", bt, lens, bs)
+            got = gpu_decode(b, pool_dev, b.step_query[step], bt, lens)
+            if step in (0, 8, 24, 32):
+                assert np.array_equal(host_bits(pool_dev).reshape(pool.shape), pool), step
+                assert_decode_close(got, oracle_decode(b, pool, b.step_query[step], bt, lens), b)
+        assert np.array_equal(host_bits(pool_dev).reshape(pool.shape), pool)
+
+
+def test_llama7b_full_size_sampled():
+    b = make_llama7b()
+    bt, lens = b.block_table_array(), b.context_lens
+    pool_dev = dev_pool(b.kv_pool, "f16")
+    got = gpu_decode(b, pool_dev, b.query, bt, lens)
+    seqs = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 19, 31]
+    ref = oracle_decode(b, b.kv_pool, b.query, bt, lens, seqs=seqs)
+    assert_decode_close(got, ref, b, seqs=seqs)
