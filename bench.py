@@ -74,6 +74,31 @@ def counter_traffic(config: str, partition: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def stream_read_gbs(torch, nbytes: int = 4 << 30, reps: int = 10) -> float:
+    """HBM read bandwidth a plain streaming kernel reaches on this device."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(REPO, "paged_kv_cache_132_amd", "libpa_bench.so"))
+    lib.pa_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_bench_read_grid.restype = ctypes.c_int
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(lib.pa_bench_read_grid(), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        lib.pa_bench_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        if lib.pa_bench_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream) != 0:
+            raise RuntimeError("pa_bench_read launch failed")
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def build_workload(name: str):
     from workloads import CONFIG_MAKERS
 
@@ -243,6 +268,8 @@ def main() -> int:
         f"p90 {np.percentile(decode_ms, 90) * 1e3:.1f}); write mean {write_ms.mean() * 1e3:.1f} us; "
         f"step {ms_step * 1e3:.1f} us")
     traffic = counter_traffic(args.config, partition)
+    achievable = stream_read_gbs(torch)
+    log(f"streaming-read kernel reaches {achievable:.0f} GB/s on this device")
 
     res = {
         "metric": METRIC,
@@ -266,6 +293,8 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s_per_layer": round(b.num_seqs / (ms_step * 1e-3), 1),
         "decode_kernel_us": round(dec_us, 2),
+        "hbm_read_achievable_gbs": round(achievable, 1),
+        "decode_frac_of_achievable": round(achieved / achievable, 4),
         "write_kernel_us": round(float(write_ms.mean() * 1e3), 2),
         "roofline": {
             "bound": "hbm",

@@ -154,8 +154,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  *                         It must be zero-filled before its first use; every call that
  *                         completes leaves it zero-filled again where it matters (the
  *                         arrival counters), so one zeroed workspace serves any number
- *                         of successive calls.  Calls that may run concurrently need
- *                         separate workspaces.
+ *                         of successive calls with the SAME size arguments.  Reusing it
+ *                         for calls with other sizes needs a fresh zero fill (the counter
+ *                         region of one layout may overlap another's partial results).
+ *                         Calls that may run concurrently need separate workspaces.
  *
  * The pass is a single kernel: workgroups own (sequence, group of KV heads,
  * partition); the last workgroup of a sequence to finish merges the

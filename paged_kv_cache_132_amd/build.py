@@ -17,8 +17,10 @@ REPO = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(REPO, "include")
 LIB = os.path.join(PKG, "libpa.so")
+BENCH_LIB = os.path.join(PKG, "libpa_bench.so")
 
 SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip"]
+BENCH_SOURCES = ["bench_util.hip"]
 
 
 def hipcc() -> str:
@@ -28,15 +30,15 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def _compile(sources, out, verbose):
+    tmp = out + ".tmp"
     cmd = [
         hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-x", "hip",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",
         f"-I{INCLUDE}", f"-I{CSRC}",
-        *[os.path.join(CSRC, s) for s in SOURCES],
+        *[os.path.join(CSRC, s) for s in sources],
         "-o", tmp,
     ]
     if verbose:
@@ -44,14 +46,20 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libpa.so")
+        raise RuntimeError(f"hipcc failed to build {os.path.basename(out)}")
     if verbose and res.stderr.strip():
         # the host pass does not know the packed-fp32 feature; that warning is harmless
         lines = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
         if lines:
             print("\n".join(lines))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libpa.so (the decode path) and libpa_bench.so (measurement helpers)."""
+    _compile(BENCH_SOURCES, BENCH_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,68 @@
+// Streaming read and copy kernels used only for measurement: the achievable
+// HBM read bandwidth on this device, and a copy of known size to calibrate
+// hardware byte counters.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "pa_bench.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGrid = 256 * 8;          // 8 workgroups per CU on a 256-CU part
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(kThreads) void read_kernel(const uint4* __restrict__ src, size_t n16,
+                                                        uint32_t* __restrict__ sink) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = src[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t red[kThreads];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] ^= red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                        size_t n16) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_bench_read_grid(void) { return kGrid; }
+
+int pa_bench_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (!src || !sink || (bytes & 15)) return -1;
+    hipLaunchKernelGGL(read_kernel, dim3(kGrid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint4*>(src), bytes / 16, sink);
+    return (int)hipGetLastError();
+}
+
+int pa_bench_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!src || !dst || (bytes & 15)) return -1;
+    hipLaunchKernelGGL(copy_kernel, dim3(kGrid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint4*>(dst), static_cast<const uint4*>(src), bytes / 16);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

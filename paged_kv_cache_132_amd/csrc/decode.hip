@@ -211,11 +211,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     // ---- the partition's token range and this lane's K/V addressing -------
     const int t_begin = p * a.partition;
     const int t_end = min(L, t_begin + a.partition);
-    const int n_chunks = (t_end - t_begin + TPC - 1) / TPC;
-    const int64_t row_stride = (int64_t)a.num_kv_heads * D;              // elements per token row
-    const int64_t half_stride = row_stride << a.block_shift;             // K half -> V half
+    const int shift = a.block_shift;
+    const uint32_t row_bytes = (uint32_t)(a.num_kv_heads * D * KVB);        // one token row, all heads
+    const uint32_t half_bytes = row_bytes << shift;                       // K half -> V half
+    const uint32_t lane_off = (uint32_t)((g * D + j * EPL) * KVB);         // this lane's 16 bytes
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
-    const int64_t lane_off = ((int64_t)g * D + j * EPL) * KVB;           // bytes within a token row
     const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
     float m[G], l[G], o[G][EPL];
@@ -226,29 +226,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[gi][e] = 0.f;
     }
-
-    // Issue the 4 K rows and 4 V rows of chunk c into kr / vr.  Returns the
-    // number of valid tokens (0 when the block id is outside the pool).
-    auto load_chunk = [&](int c, uint4 (&kr)[TPC], uint4 (&vr)[TPC]) -> int {
-        const int tc = t_begin + c * TPC;
-        const int blk = bt_row[tc >> a.block_shift];
-        const int nvalid = (blk >= 0 && blk < a.num_blocks) ? min(TPC, t_end - tc) : 0;
-        const int blk_safe = nvalid ? blk : 0;
-        const int off = tc & (a.block_size - 1);
-        const uint8_t* kbase =
-            pool + (((int64_t)blk_safe * 2 << a.block_shift) + off) * row_stride * KVB + lane_off;
-#pragma unroll
-        for (int i = 0; i < TPC; ++i) {
-            const int ii = i < nvalid ? i : 0;
-            kr[i] = *reinterpret_cast<const uint4*>(kbase + ii * row_stride * KVB);
-        }
-#pragma unroll
-        for (int i = 0; i < TPC; ++i) {
-            const int ii = i < nvalid ? i : 0;
-            vr[i] = *reinterpret_cast<const uint4*>(kbase + (half_stride + ii * row_stride) * KVB);
-        }
-        return nvalid;
-    };
 
     auto compute_chunk = [&](int nvalid, const uint4 (&kr)[TPC], const uint4 (&vr)[TPC]) {
         if (nvalid <= 0) return;
@@ -282,23 +259,55 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         }
     };
 
-    // ---- main loop: two chunks in flight per wave --------------------------
-    {
+    // ---- main loop --------------------------------------------------------
+    // The partition is walked in segments of up to 64 logical blocks.  Each
+    // wave holds the segment's physical block ids in one VGPR (lane k = entry
+    // k) and picks them out with readlane, so no memory access sits between
+    // one chunk's loads and the next.  Chunks of 4 tokens go round-robin to
+    // the 4 waves; every wave keeps two chunks of loads in flight (A and B),
+    // issuing chunk c+8 right after it has consumed chunk c.  Loads past the
+    // wave's last chunk re-read a valid chunk and are masked out (nvalid 0).
+    const int lb_first = t_begin >> shift;
+    const int lb_last = (t_end - 1) >> shift;
+    for (int seg0 = lb_first; seg0 <= lb_last; seg0 += 64) {
+        const int seg_blocks = min(64, lb_last - seg0 + 1);
+        const int my_blk = lane < seg_blocks ? bt_row[seg0 + lane] : 0;
+        const int seg_t0 = max(t_begin, seg0 << shift);
+        const int seg_t1 = min(t_end, (seg0 + seg_blocks) << shift);
+        const int n_chunks = (seg_t1 - seg_t0 + TPC - 1) / TPC;
+        if (wave >= n_chunks) continue;
+        const int n_mine = (n_chunks - wave + NW - 1) / NW;
+
+        auto issue = [&](int c, uint4 (&kr)[TPC], uint4 (&vr)[TPC]) -> int {
+            const int cc = min(c, n_chunks - 1);
+            const int tc = seg_t0 + cc * TPC;
+            const int blk = __builtin_amdgcn_readlane(my_blk, (tc >> shift) - seg0);
+            const bool blk_ok = blk >= 0 && blk < a.num_blocks;
+            const int nvalid = (c < n_chunks && blk_ok) ? min(TPC, seg_t1 - tc) : 0;
+            const int64_t row0 = ((int64_t)(blk_ok ? blk : 0) * 2 << shift) + (tc & (a.block_size - 1));
+            const uint8_t* kbase = pool + row0 * row_bytes;
+#pragma unroll
+            for (int i = 0; i < TPC; ++i) {
+                const uint32_t ti = (uint32_t)(i < nvalid ? i : 0) * row_bytes;
+                kr[i] = *reinterpret_cast<const uint4*>(kbase + ti + lane_off);
+            }
+#pragma unroll
+            for (int i = 0; i < TPC; ++i) {
+                const uint32_t ti = (uint32_t)(i < nvalid ? i : 0) * row_bytes;
+                vr[i] = *reinterpret_cast<const uint4*>(kbase + half_bytes + ti + lane_off);
+            }
+            return nvalid;
+        };
+
         uint4 ka[TPC], va[TPC], kb[TPC], vb[TPC];
         int c = wave;
-        if (c < n_chunks) {
-            int na = load_chunk(c, ka, va);
-            while (true) {
-                int nb = 0;
-                if (c + NW < n_chunks) nb = load_chunk(c + NW, kb, vb);
-                compute_chunk(na, ka, va);
-                c += NW;
-                if (c >= n_chunks) break;
-                if (c + NW < n_chunks) na = load_chunk(c + NW, ka, va);
-                compute_chunk(nb, kb, vb);
-                c += NW;
-                if (c >= n_chunks) break;
-            }
+        int na = issue(c, ka, va);
+        for (int it = 0; it < n_mine; it += 2) {
+            const int nb = issue(c + NW, kb, vb);
+            compute_chunk(na, ka, va);
+            na = issue(c + 2 * NW, ka, va);
+            compute_chunk(nb, kb, vb);
+            c += 2 * NW;
         }
     }
 
