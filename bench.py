@@ -99,6 +99,24 @@ def stream_read_gbs(torch, nbytes: int = 4 << 30, reps: int = 10) -> float:
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def copy_calibration(torch, reps: int, nbytes: int = 1 << 30) -> int:
+    """Run a plain 1 GiB device copy `reps` times: a kernel whose HBM traffic is
+    known exactly (nbytes read + nbytes written), to scale byte counters."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(REPO, "paged_kv_cache_132_amd", "libpa_bench.so"))
+    lib.pa_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(reps):
+        if lib.pa_bench_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream) != 0:
+            raise RuntimeError("pa_bench_copy launch failed")
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+    return 0
+
+
 def build_workload(name: str):
     from workloads import CONFIG_MAKERS
 
@@ -203,6 +221,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 1 GiB copy kernel --steps times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
@@ -216,6 +236,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     pa.load()
+    if args.copy_calibration:
+        return copy_calibration(torch, args.steps)
     log(f"building workload {args.config}")
     b = build_workload(args.config)
     nbytes = algorithmic_bytes(b)

@@ -123,8 +123,7 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t nu
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs with
  * the same arguments (same `partition_size`).  Returns 0 for invalid
- * arguments.  The workspace holds per-partition partial results and one
- * arrival counter per (sequence, KV-head group).
+ * arguments.  The workspace holds per-partition partial results.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size,
@@ -150,19 +149,15 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  *   partition_size        0 = library choice, else a positive multiple of block_size:
  *                         tokens per split-K partition (a sequence shorter than one
  *                         partition is not split)
- *   workspace     in/out  device memory of at least pa_decode_workspace_size(...) bytes.
- *                         It must be zero-filled before its first use; every call that
- *                         completes leaves it zero-filled again where it matters (the
- *                         arrival counters), so one zeroed workspace serves any number
- *                         of successive calls with the SAME size arguments.  Reusing it
- *                         for calls with other sizes needs a fresh zero fill (the counter
- *                         region of one layout may overlap another's partial results).
- *                         Calls that may run concurrently need separate workspaces.
+ *   workspace     scratch device memory of at least pa_decode_workspace_size(...) bytes
+ *                         for per-partition partial results.  Its contents on entry do not
+ *                         matter.  Calls that may run concurrently need separate workspaces.
  *
- * The pass is a single kernel: workgroups own (sequence, group of KV heads,
- * partition); the last workgroup of a sequence to finish merges the
- * partitions' partial softmax states.  Output does not depend on which
- * physical blocks the table names, only on their logical order.
+ * Two kernels on `stream`: workgroups of the first own (sequence, group of KV
+ * heads, partition) and write either the final output (single-partition
+ * sequences) or a partial softmax state; the second merges the partials of
+ * split sequences.  Output does not depend on which physical blocks the
+ * table names, only on their logical order.
  */
 pa_status pa_decode(void* out, const void* query, pa_dtype q_dtype,
                     const void* kv_pool, pa_dtype kv_dtype,

@@ -133,30 +133,18 @@ def decode_partition_size(num_seqs: int, num_heads: int, num_kv_heads: int, head
 
 
 class Workspace:
-    """A zero-filled device workspace for pa_decode, grown on demand.
+    """A device workspace for pa_decode, grown on demand (its contents on
+    entry do not matter, so one buffer serves calls of any size on one stream)."""
 
-    pa_decode leaves the workspace's arrival counters at zero after every
-    completed call, so one buffer serves successive calls of one size on one
-    stream; when the requested size changes the buffer is zero-filled again."""
-
-    def __init__(self, device=None):
-        self.device = device
+    def __init__(self):
         self.buf: torch.Tensor | None = None
-        self.layout = None
 
-    def get(self, nbytes: int, device, layout=None) -> torch.Tensor:
-        layout = nbytes if layout is None else layout
+    def get(self, nbytes: int, device) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        elif self.layout != layout:
-            self.buf.zero_()
-        self.layout = layout
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         return self.buf
 
 
-# One zero-filled workspace per (device, argument set).  A workspace must not
-# be shared between calls of different sizes without re-zeroing it: the
-# counter region of one layout can overlap another layout's partial results.
 _default_ws: dict = {}
 
 
@@ -176,15 +164,10 @@ def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tenso
         raise ValueError("out must match query")
     kvt = pa_dtype(kv_pool)
     need = decode_workspace_size(B, hq, hkv, d, bs, mb, kvt, partition_size)
-    key = (query.device, B, hq, hkv, d, bs, mb, kvt, int(partition_size))
     if workspace is None:
-        workspace = _default_ws.get(key)
-        if workspace is None:
-            if len(_default_ws) > 64:
-                _default_ws.clear()
-            workspace = _default_ws.setdefault(key, Workspace())
+        workspace = _default_ws.setdefault((query.device, torch.cuda.current_stream().cuda_stream), Workspace())
     if isinstance(workspace, Workspace):
-        ws = workspace.get(need, query.device, key)
+        ws = workspace.get(need, query.device)
     else:
         ws = workspace
     st = load().pa_decode(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), kvt,

@@ -1,7 +1,7 @@
-// pa_decode kernel: paged decode attention in one pass with split-K and an
-// in-kernel merge ([nano-vllm blog §2.3], [CANN notes §4.3 step 4]; the
-// FlashAttention-style tiling of the computation inside a paged layout that
-// [nano-vllm blog §2.3] says composes with paging).
+// pa_decode kernels: paged decode attention with split-K over token
+// partitions and a second merge pass ([nano-vllm blog §2.3], [CANN notes §4.3
+// step 4]; the FlashAttention-style tiling of the computation inside a paged
+// layout that [nano-vllm blog §2.3] says composes with paging).
 //
 // Work decomposition
 //   A workgroup (4 waves) owns one (sequence, group of KV heads, partition of
@@ -29,12 +29,13 @@
 //   PV:   o[e] += p * v[e] in float32 for the lane's slice of head_dim.
 //
 // End of the workgroup: the 4 waves' states are merged through LDS.  A
-// sequence with a single partition writes its output directly.  Otherwise
-// the workgroup stores its partial (max, sum, unnormalised o), publishes it
-// with a device-scope fence and bumps the (sequence, group) arrival counter;
-// the workgroup that arrives last merges all partitions
-//     M = max_p m_p,  out = sum_p 2^(m_p-M) o_p / sum_p 2^(m_p-M) l_p
-// writes the output and resets the counter to zero for the next call.
+// sequence with a single partition writes its output directly; otherwise the
+// workgroup stores its partial (max, sum, unnormalised o) in the workspace
+// and the merge kernel, launched next on the same stream, combines them
+//     M = max_p m_p,  out = sum_p 2^(m_p-M) o_p / sum_p 2^(m_p-M) l_p.
+// Two launches instead of a last-arriving-workgroup merge: publishing
+// partials between workgroups inside one kernel needs device-scope fences,
+// and on this part each one writes back and invalidates the XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -143,6 +144,9 @@ __device__ __forceinline__ void accumulate_v(float (&o)[EPL], float p, const uin
     }
 }
 
+template <int QT, int D, int NE>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h, int d0, int n_part);
+
 template <int QT, int KVT, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     constexpr int KVB = KVT == PA_FP8_E4M3 ? 1 : 2;
@@ -157,7 +161,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     __shared__ float s_m[NW][ROWS];
     __shared__ float s_l[NW][ROWS];
     __shared__ float s_o[NW][64 * EPL];
-    __shared__ int s_last;
 
     // ---- which (sequence, KV-head group, partition) -------------------------
     const int wg = blockIdx.x;
@@ -369,45 +372,50 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         }
         __syncthreads();
     }
-    if (n_part == 1) return;
+}
 
-    // ---- split-K: the last partition to arrive merges ----------------------
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const int old = atomicAdd(&a.counters[s * a.groups + group], 1);
-        s_last = (old == n_part - 1);
+// Split-K merge of one sequence's partitions for NE consecutive output
+// elements [d0, d0 + NE) of query head h:
+//     M = max_p m_p,  out = v_scale * sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+template <int QT, int D, int NE>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h, int d0, int n_part) {
+    const int64_t base = ((int64_t)s * a.num_heads + h) * a.max_partitions;
+    const float* ml = a.part_ml + base * 2;
+    const float* po = a.part_o + base * D + d0;
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int pp = 0; pp < n_part; ++pp) M = fmaxf(M, ml[pp * 2]);
+    float den = 0.f;
+    float num[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) num[e] = 0.f;
+#pragma unroll 4
+    for (int pp = 0; pp < n_part; ++pp) {
+        const float f = fast_exp2(ml[pp * 2] - M);
+        den = fmaf(f, ml[pp * 2 + 1], den);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) num[e] = fmaf(f, po[(int64_t)pp * D + e], num[e]);
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    const float inv = a.v_scale / den;
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + h) * D + d0;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) dst[e] = to_out_bits<QT>(num[e] * inv);
+}
 
-    if (m_ok) {
-#pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-            const int h = mg_row * G + gi;
-            const int64_t base = ((int64_t)s * Hq + h) * P;
-            float M = -INFINITY;
-            for (int pp = 0; pp < n_part; ++pp) M = fmaxf(M, a.part_ml[(base + pp) * 2]);
-            float den = 0.f;
-            float num[OPT];
-#pragma unroll
-            for (int e = 0; e < OPT; ++e) num[e] = 0.f;
-            const int d0 = mj * EPL + part * OPT;
-            for (int pp = 0; pp < n_part; ++pp) {
-                const float f = fast_exp2(a.part_ml[(base + pp) * 2] - M);
-                den = fmaf(f, a.part_ml[(base + pp) * 2 + 1], den);
-                const float* po = a.part_o + (base + pp) * D + d0;
-#pragma unroll
-                for (int e = 0; e < OPT; ++e) num[e] = fmaf(f, po[e], num[e]);
-            }
-            const float inv = a.v_scale / den;
-            uint16_t* dst = out + ((int64_t)s * Hq + h) * D + d0;
-#pragma unroll
-            for (int e = 0; e < OPT; ++e) dst[e] = to_out_bits<QT>(num[e] * inv);
-        }
-    }
-    if (tid == 0) atomicExch(&a.counters[s * a.groups + group], 0);
+// Second pass of split-K: one thread per output element of every sequence
+// that was split into more than one partition.
+template <int QT, int D>
+__global__ __launch_bounds__(kDecodeThreads) void merge_kernel(DecodeArgs a) {
+    constexpr int HPB = kDecodeThreads / D;          // query heads per workgroup
+    const int chunks = (a.num_heads + HPB - 1) / HPB;
+    const int s = blockIdx.x / chunks;
+    const int h = (blockIdx.x % chunks) * HPB + threadIdx.x / D;
+    const int d = threadIdx.x % D;
+    const int max_tokens = a.max_blocks_per_seq << a.block_shift;
+    const int L = min(a.context_lens[s], max_tokens);
+    const int n_part = L > 0 ? (L + a.partition - 1) / a.partition : 0;
+    if (n_part <= 1 || h >= a.num_heads) return;
+    merge_partials<QT, D, 1>(a, s, h, d, n_part);
 }
 
 template <int QT, int KVT, int D>
@@ -419,6 +427,10 @@ int launch_d(const DecodeArgs& a, const DecodePlan& plan, int group_size, hipStr
         case 4: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 4>), grid, block, 0, st, a); break;
         case 8: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 8>), grid, block, 0, st, a); break;
         default: return (int)hipErrorInvalidValue;
+    }
+    if (plan.max_partitions > 1) {
+        const int chunks = (a.num_heads + kDecodeThreads / D - 1) / (kDecodeThreads / D);
+        hipLaunchKernelGGL((merge_kernel<QT, D>), dim3((unsigned)(a.num_seqs * chunks)), block, 0, st, a);
     }
     return (int)hipGetLastError();
 }

@@ -102,10 +102,8 @@ bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
     p.max_partitions = (int)((max_tokens + part - 1) / part);
     p.grid = (int64_t)p.groups * num_seqs * p.max_partitions;
     if (p.grid > INT32_MAX) return false;
-    const size_t n_cnt = (size_t)num_seqs * p.groups;
     const size_t n_part = (size_t)num_seqs * num_heads * p.max_partitions;
-    p.off_counters = 0;
-    p.off_ml = align_up(n_cnt * sizeof(int32_t), 256);
+    p.off_ml = 0;
     p.off_o = p.off_ml + align_up(n_part * 2 * sizeof(float), 256);
     p.bytes = p.off_o + align_up(n_part * (size_t)head_dim * sizeof(float), 256);
     if (p.bytes == 0) p.bytes = 256;
@@ -222,7 +220,6 @@ pa_status pa_decode(void* out, const void* query, pa_dtype q_dtype, const void* 
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     char* ws = static_cast<char*>(workspace);
-    a.counters = reinterpret_cast<int32_t*>(ws + plan.off_counters);
     a.part_ml = reinterpret_cast<float*>(ws + plan.off_ml);
     a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.num_seqs = num_seqs;

@@ -34,7 +34,7 @@ struct DecodePlan {
     int partition;       // tokens per split-K partition (multiple of block_size)
     int max_partitions;  // ceil(max_blocks_per_seq * block_size / partition)
     int64_t grid;        // workgroups launched
-    size_t off_counters, off_ml, off_o, bytes;   // workspace layout
+    size_t off_ml, off_o, bytes;   // workspace layout
 };
 
 // Pure argument checks (no HIP calls): shared by the API and the CPU tests.
@@ -55,7 +55,6 @@ struct DecodeArgs {
     const void* kv_pool;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    int32_t* counters;      // [num_seqs * groups]
     float* part_ml;         // [num_seqs, num_heads, max_partitions, 2] (max, sum) log2 domain
     float* part_o;          // [num_seqs, num_heads, max_partitions, head_dim]
     int32_t num_seqs, num_heads, num_kv_heads;
