@@ -11,23 +11,35 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kGrid = 256 * 8;          // 8 workgroups per CU on a 256-CU part
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kUnroll = 8;
 
-__global__ __launch_bounds__(kThreads) void read_kernel(const uint4* __restrict__ src, size_t n16,
+// Each workgroup streams one contiguous slice with nontemporal 16-byte loads,
+// kUnroll loads per thread in flight (the fastest plain read found on this
+// part).  Bytes past the last full slice are read by workgroup 0.
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ src, size_t n16,
                                                         uint32_t* __restrict__ sink) {
-    const size_t stride = (size_t)gridDim.x * kThreads;
-    size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    const size_t per = n16 / gridDim.x;
+    const u32x4* p = src + blockIdx.x * per;
     uint32_t acc = 0;
-    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
-        uint4 v[kUnroll];
+    size_t i = threadIdx.x;
+    for (; i + (kUnroll - 1) * kThreads < per; i += kUnroll * kThreads) {
+        u32x4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+        for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kThreads);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
-    for (; i < n16; i += stride) {
-        const uint4 v = src[i];
+    for (; i < per; i += kThreads) {
+        const u32x4 v = __builtin_nontemporal_load(p + i);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (blockIdx.x == 0) {
+        for (size_t k = per * gridDim.x + threadIdx.x; k < n16; k += kThreads) {
+            const u32x4 v = src[k];
+            acc ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
     }
     __shared__ uint32_t red[kThreads];
     red[threadIdx.x] = acc;
@@ -54,7 +66,7 @@ int pa_bench_read_grid(void) { return kGrid; }
 int pa_bench_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
     if (!src || !sink || (bytes & 15)) return -1;
     hipLaunchKernelGGL(read_kernel, dim3(kGrid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint4*>(src), bytes / 16, sink);
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
     return (int)hipGetLastError();
 }
 

@@ -47,8 +47,10 @@ namespace {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTokensPerChunk = 4;
+constexpr int kTokensPerChunk = 4;   // tokens one wave takes per step
+constexpr int kStages = 2;           // chunks of loads each wave keeps in flight
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -70,6 +72,12 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// K/V rows are read exactly once per call: load them with the nontemporal
+// hint so the stream does not displace other lines in L2 and the MALL.
+__device__ __forceinline__ uint4 stream_load(const uint8_t* p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -156,6 +164,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     constexpr int QDW = EPL / 2;            // packed 16-bit query pairs per lane
     constexpr int NW = kDecodeWaves;
     constexpr int TPC = kTokensPerChunk;
+    constexpr int NS = kStages;
     constexpr int OPT = EPL / NW;           // output elements per thread in the merge
 
     __shared__ float s_m[NW][ROWS];
@@ -266,9 +275,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     // The partition is walked in segments of up to 64 logical blocks.  Each
     // wave holds the segment's physical block ids in one VGPR (lane k = entry
     // k) and picks them out with readlane, so no memory access sits between
-    // one chunk's loads and the next.  Chunks of 4 tokens go round-robin to
-    // the 4 waves; every wave keeps two chunks of loads in flight (A and B),
-    // issuing chunk c+8 right after it has consumed chunk c.  Loads past the
+    // one chunk's loads and the next.  Chunks of TPC tokens go round-robin to
+    // the 4 waves; every wave keeps NS chunks of loads in flight, issuing
+    // chunk c + (NS-1)*4 right before it consumes chunk c.  Loads past the
     // wave's last chunk re-read a valid chunk and are masked out (nvalid 0).
     const int lb_first = t_begin >> shift;
     const int lb_last = (t_end - 1) >> shift;
@@ -292,25 +301,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < TPC; ++i) {
                 const uint32_t ti = (uint32_t)(i < nvalid ? i : 0) * row_bytes;
-                kr[i] = *reinterpret_cast<const uint4*>(kbase + ti + lane_off);
+                kr[i] = stream_load(kbase + ti + lane_off);
             }
 #pragma unroll
             for (int i = 0; i < TPC; ++i) {
                 const uint32_t ti = (uint32_t)(i < nvalid ? i : 0) * row_bytes;
-                vr[i] = *reinterpret_cast<const uint4*>(kbase + half_bytes + ti + lane_off);
+                vr[i] = stream_load(kbase + half_bytes + ti + lane_off);
             }
             return nvalid;
         };
 
-        uint4 ka[TPC], va[TPC], kb[TPC], vb[TPC];
+        uint4 kr[NS][TPC], vr[NS][TPC];
+        int nv[NS];
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st) nv[st] = issue(wave + st * NW, kr[st], vr[st]);
         int c = wave;
-        int na = issue(c, ka, va);
-        for (int it = 0; it < n_mine; it += 2) {
-            const int nb = issue(c + NW, kb, vb);
-            compute_chunk(na, ka, va);
-            na = issue(c + 2 * NW, ka, va);
-            compute_chunk(nb, kb, vb);
-            c += 2 * NW;
+        for (int it = 0; it < n_mine; it += NS) {
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const int nxt = (st + NS - 1) % NS;
+                nv[nxt] = issue(c + (NS - 1) * NW, kr[nxt], vr[nxt]);
+                compute_chunk(nv[st], kr[st], vr[st]);
+                c += NW;
+            }
         }
     }
 
@@ -382,19 +395,24 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
     const int64_t base = ((int64_t)s * a.num_heads + h) * a.max_partitions;
     const float* ml = a.part_ml + base * 2;
     const float* po = a.part_o + base * D + d0;
+    // One pass with a running maximum: every partition's loads are
+    // independent of the others, so they are all in flight together.
     float M = -INFINITY;
-#pragma unroll 8
-    for (int pp = 0; pp < n_part; ++pp) M = fmaxf(M, ml[pp * 2]);
     float den = 0.f;
     float num[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) num[e] = 0.f;
 #pragma unroll 4
     for (int pp = 0; pp < n_part; ++pp) {
-        const float f = fast_exp2(ml[pp * 2] - M);
-        den = fmaf(f, ml[pp * 2 + 1], den);
+        const float mp = ml[pp * 2];
+        const float lp = ml[pp * 2 + 1];
+        const float m_new = fmaxf(M, mp);
+        const float alpha = fast_exp2(M - m_new);      // 0 on the first partition
+        const float f = fast_exp2(mp - m_new);
+        den = fmaf(den, alpha, f * lp);
 #pragma unroll
-        for (int e = 0; e < NE; ++e) num[e] = fmaf(f, po[(int64_t)pp * D + e], num[e]);
+        for (int e = 0; e < NE; ++e) num[e] = fmaf(num[e], alpha, f * po[(int64_t)pp * D + e]);
+        M = m_new;
     }
     const float inv = a.v_scale / den;
     uint16_t* dst = static_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + h) * D + d0;
