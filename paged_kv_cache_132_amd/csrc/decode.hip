@@ -446,10 +446,13 @@ int launch_d(const DecodeArgs& a, const DecodePlan& plan, int group_size, hipStr
         case 8: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 8>), grid, block, 0, st, a); break;
         default: return (int)hipErrorInvalidValue;
     }
-    if (plan.max_partitions > 1) {
-        const int chunks = (a.num_heads + kDecodeThreads / D - 1) / (kDecodeThreads / D);
-        hipLaunchKernelGGL((merge_kernel<QT, D>), dim3((unsigned)(a.num_seqs * chunks)), block, 0, st, a);
-    }
+    return (int)hipGetLastError();
+}
+
+template <int QT, int D>
+int launch_merge(const DecodeArgs& a, hipStream_t st) {
+    const int chunks = (a.num_heads + kDecodeThreads / D - 1) / (kDecodeThreads / D);
+    hipLaunchKernelGGL((merge_kernel<QT, D>), dim3((unsigned)(a.num_seqs * chunks)), dim3(kDecodeThreads), 0, st, a);
     return (int)hipGetLastError();
 }
 
@@ -465,9 +468,15 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
                   int head_dim, int group_size, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (plan.grid == 0) return 0;
-    if (kv_dtype == PA_F16) return launch_t<PA_F16, PA_F16>(a, plan, head_dim, group_size, st);
-    if (kv_dtype == PA_BF16) return launch_t<PA_BF16, PA_BF16>(a, plan, head_dim, group_size, st);
-    return launch_t<PA_BF16, PA_FP8_E4M3>(a, plan, head_dim, group_size, st);
+    int err;
+    if (plan.geo.mfma) err = launch_decode_gqa_mfma(a, plan, group_size, stream);
+    else if (kv_dtype == PA_F16) err = launch_t<PA_F16, PA_F16>(a, plan, head_dim, group_size, st);
+    else if (kv_dtype == PA_BF16) err = launch_t<PA_BF16, PA_BF16>(a, plan, head_dim, group_size, st);
+    else err = launch_t<PA_BF16, PA_FP8_E4M3>(a, plan, head_dim, group_size, st);
+    if (err != 0 || plan.max_partitions <= 1) return err;
+    const bool f16 = q_dtype == PA_F16;
+    if (head_dim == 64) return f16 ? launch_merge<PA_F16, 64>(a, st) : launch_merge<PA_BF16, 64>(a, st);
+    return f16 ? launch_merge<PA_F16, 128>(a, st) : launch_merge<PA_BF16, 128>(a, st);
 }
 
 }  // namespace pa

@@ -1,0 +1,317 @@
+// pa_decode for grouped-query attention over an fp8 (OCP e4m3) KV cache on
+// the matrix cores ([nano-vllm blog §2.3] decode attention; fp8 KV of
+// [nano-vllm blog §1.1, §6.3]).  Several query heads (G = 2, 4 or 8) read one
+// KV head, so QK and PV become small dense products per 32-token step; the
+// 4-to-8 multiply-adds per KV byte that would saturate the vector ALUs run on
+// v_mfma_f32_16x16x32_bf16 instead, and the kernel stays bound by HBM.
+//
+// Work decomposition
+//   Workgroup = (sequence, group of 4 KV heads, partition); wave w owns KV
+//   head 4*group + w for the whole partition, so the waves never exchange
+//   softmax state.  A wave walks its partition in steps of 32 tokens (two
+//   16-token halves; a half never crosses a block boundary for block size 16
+//   or 32), keeping two steps of K/V loads in flight.
+//
+// Per step, per wave (lane l: n = l % 16, q = l / 16):
+//   QK   A = K rows: lane (token n of the half, bytes 32q..32q+31 of the head's
+//        128-byte row), widened fp8 -> bf16 (exact); B = query: lane (head n,
+//        head_dim 32q..32q+31), zero for n >= G.  4 MFMAs per half give
+//        S[token][head] with lane (q, n) holding tokens 4q..4q+3 of head n.
+//   soft running max over the 32 tokens (in-lane, then across the 4 rows),
+//        exp2-domain probabilities; masked tokens get weight 0.
+//   PV   A = P: exactly the lane's own 8 probabilities (k-slot 8q+j is token
+//        4q+j of half 0 for j < 4, token 4q+j-4 of half 1 for j >= 4), bf16.
+//        B = V: the 32 V rows are staged in LDS and read back transposed with
+//        ds_read_tr8_b64 -- within each 16-lane group, lane i receives byte
+//        (i & 7) of the 8 rows addressed by lanes 2j + (i >> 3) -- so each lane
+//        gets the 8 k-slot tokens of one head_dim column, widened to bf16.
+//        8 MFMAs (16 head_dim columns each) accumulate O[head][d] in fp32.
+//
+// Output, partials and the merge are shared with the vector kernel.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;                  // head_dim
+constexpr int kRowStride = 144;          // LDS bytes per staged V row (128 + 16 against bank conflicts)
+constexpr int kStepTokens = 32;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint4 stream_load(const uint8_t* p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
+// 8 fp8 codes (two dwords) -> 8 bf16, exactly.
+__device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    const uint32_t b = __float_as_uint(x);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int m) {
+    const int lane = __lane_id();
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float from_lane(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
+template <int G>
+__global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(DecodeArgs a) {
+    static_assert(G == 2 || G == 4 || G == 8, "query heads per KV head");
+    constexpr int NW = kDecodeWaves;
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[NW][kStepTokens * kRowStride];
+
+    const int wg = blockIdx.x;
+    const int group = wg % a.groups;
+    const int rest = wg / a.groups;
+    const int s = rest % a.num_seqs;
+    const int p = rest / a.num_seqs;
+    const int max_tokens = a.max_blocks_per_seq << a.block_shift;
+    const int L = min(a.context_lens[s], max_tokens);
+    const int n_part = L > 0 ? (L + a.partition - 1) / a.partition : 0;
+    if (p >= (n_part > 0 ? n_part : 1)) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = group * NW + wave;                 // this wave's KV head
+    if (g >= a.num_kv_heads) return;                 // no barriers below: idle waves may leave
+    const int n = lane & 15;
+    const int q = lane >> 4;
+    const int Hq = a.num_heads;
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+
+    if (L <= 0) {
+        uint16_t* dst = out + ((int64_t)s * Hq + g * G) * kD;
+        for (int i = lane; i < G * kD; i += 64) dst[i] = 0;
+        return;
+    }
+
+    // ---- query operand: head n of this KV head's group, head_dim 32q.. ----
+    bf16x8 qop[4];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.query) + ((int64_t)s * Hq + g * G + (n < G ? n : 0)) * kD + 32 * q;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 v = n < G ? *reinterpret_cast<const uint4*>(qp + 8 * c) : make_uint4(0, 0, 0, 0);
+            qop[c] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    const int t_begin = p * a.partition;
+    const int t_end = min(L, t_begin + a.partition);
+    const int shift = a.block_shift;
+    const uint32_t row_bytes = (uint32_t)(a.num_kv_heads * kD);               // fp8: 1 byte per element
+    const uint32_t half_bytes = row_bytes << shift;                           // K half -> V half
+    const uint32_t lane_col = (uint32_t)(g * kD + 32 * q);                    // this lane's 32 bytes of a row
+    const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
+    const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+    // LDS: this wave's V staging rows; transposed-read base address of this lane
+    uint8_t* sv = s_v[wave];
+    const int jj = n >> 1;
+    const uint32_t tr_off = (uint32_t)((16 * (jj >> 2) + 4 * q + (jj & 3)) * kRowStride + 8 * (lane & 1));
+
+    float m_run = -INFINITY;       // running max of head n (identical in all 4 rows)
+    float l_lane = 0.f;            // this lane's share of head n's running sum
+    f32x4 oacc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int lb_first = t_begin >> shift;
+    const int lb_last = (t_end - 1) >> shift;
+    for (int seg0 = lb_first; seg0 <= lb_last; seg0 += 64) {
+        const int seg_blocks = min(64, lb_last - seg0 + 1);
+        const int my_blk = lane < seg_blocks ? bt_row[seg0 + lane] : 0;
+        const int seg_t0 = max(t_begin, seg0 << shift);
+        const int seg_t1 = min(t_end, (seg0 + seg_blocks) << shift);
+        const int n_steps = (seg_t1 - seg_t0 + kStepTokens - 1) / kStepTokens;
+
+        // Issue the K and V loads of step k (two halves x 32 bytes per lane).
+        // Rows past the end are redirected to the first row of the step, which
+        // is always valid, and are masked out of the softmax.
+        auto issue = [&](int k, uint4 (&kr)[4], uint4 (&vr)[4]) {
+            const int kk = min(k, n_steps - 1);
+            const int t0 = seg_t0 + kk * kStepTokens;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int th = min(t0 + 16 * u, seg_t1 - 1) & ~15;       // half start (clamped into range)
+                const int blk = __builtin_amdgcn_readlane(my_blk, (th >> shift) - seg0);
+                const bool ok = blk >= 0 && blk < a.num_blocks;
+                const int tok = (th + n < seg_t1) ? th + n : th;
+                const int64_t row = ((int64_t)(ok ? blk : 0) * 2 << shift) + (tok & (a.block_size - 1));
+                const uint8_t* kp = pool + row * row_bytes + lane_col;
+                kr[2 * u] = stream_load(kp);
+                kr[2 * u + 1] = stream_load(kp + 16);
+                vr[2 * u] = stream_load(kp + half_bytes);
+                vr[2 * u + 1] = stream_load(kp + half_bytes + 16);
+            }
+        };
+
+        auto compute = [&](int k, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+            if (k >= n_steps) return;
+            const int t0 = seg_t0 + k * kStepTokens;
+            // block ids outside the pool drop the whole half
+            bool half_ok[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int th = t0 + 16 * u;
+                const int blk = th < seg_t1 ? __builtin_amdgcn_readlane(my_blk, (th >> shift) - seg0) : -1;
+                half_ok[u] = th < seg_t1 && blk >= 0 && blk < a.num_blocks;
+            }
+            // stage V rows (row 16u + n) for the transposed reads below
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                uint8_t* dst = sv + (16 * u + n) * kRowStride + 32 * q;
+                *reinterpret_cast<uint4*>(dst) = vr[2 * u];
+                *reinterpret_cast<uint4*>(dst + 16) = vr[2 * u + 1];
+            }
+            // QK: S[token][head] for both halves
+            f32x4 sacc[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const uint32_t w[8] = {kr[2 * u].x, kr[2 * u].y, kr[2 * u].z, kr[2 * u].w,
+                                       kr[2 * u + 1].x, kr[2 * u + 1].y, kr[2 * u + 1].z, kr[2 * u + 1].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w[2 * c], w[2 * c + 1]), qop[c], acc, 0, 0, 0);
+                sacc[u] = acc;
+            }
+            // online softmax over the step's 32 tokens (lane: tokens 4q+i of each half, head n)
+            float sc[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tt = t0 + 16 * u + 4 * q + i;
+                    const float v = (half_ok[u] && tt < seg_t1) ? sacc[u][i] * a.score_scale : -INFINITY;
+                    sc[4 * u + i] = v;
+                    mx = fmaxf(mx, v);
+                }
+            }
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            // a half whose blocks are all dropped can leave m_new at -inf for this step
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+            // probabilities rounded to bf16 once: the same values feed the PV
+            // product and the running sum, so the weights normalise exactly
+            uint16_t pb[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[e] = bf16_bits(sc[e] == -INFINITY ? 0.f : fast_exp2(sc[e] - m_new));
+                psum += __uint_as_float((uint32_t)pb[e] << 16);
+            }
+            l_lane = l_lane * alpha + psum;
+            m_run = m_new;
+            // rescale O rows (head 4q+i in register i) when some real head's max moved
+            if (__builtin_amdgcn_ballot_w64(n < G && alpha != 1.f)) {
+                float ar[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ar[i] = from_lane(alpha, 4 * q + i);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oacc[t][i] *= ar[i];
+                }
+            }
+            // PV
+            bf16x8 pop;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pop[e] = __builtin_bit_cast(__bf16, pb[e]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2*)(sv + tr_off + 16 * t));
+                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, widen8((uint32_t)v8[0], (uint32_t)v8[1]),
+                                                                oacc[t], 0, 0, 0);
+            }
+        };
+
+        uint4 ka[4], va[4], kb[4], vb[4];
+        issue(0, ka, va);
+        for (int k = 0; k < n_steps; k += 2) {
+            issue(k + 1, kb, vb);
+            compute(k, ka, va);
+            issue(k + 2, ka, va);
+            compute(k + 1, kb, vb);
+        }
+    }
+
+    // ---- finish: per-head sums, then the output or a split-K partial -------
+    l_lane += shfl_xor(l_lane, 16);
+    l_lane += shfl_xor(l_lane, 32);
+    const int P = a.max_partitions;
+    float lr[4], mr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lr[i] = from_lane(l_lane, 4 * q + i);
+        mr[i] = from_lane(m_run, 4 * q + i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int hl = 4 * q + i;                     // head within the group
+        if (hl >= G) continue;
+        const int h = g * G + hl;
+        if (n_part == 1) {
+            const float inv = a.v_scale / lr[i];
+            uint16_t* dst = out + ((int64_t)s * Hq + h) * kD + n;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dst[16 * t] = bf16_bits(oacc[t][i] * inv);
+        } else {
+            const int64_t slot = ((int64_t)s * Hq + h) * P + p;
+            float* po = a.part_o + slot * kD + n;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) po[16 * t] = oacc[t][i];
+            if (n == 0) {
+                a.part_ml[slot * 2] = mr[i];
+                a.part_ml[slot * 2 + 1] = lr[i];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool gqa_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int group_size) {
+    return q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3 && head_dim == kD &&
+           (group_size == 2 || group_size == 4 || group_size == 8);
+}
+
+int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)plan.grid), block(kDecodeThreads);
+    switch (group_size) {
+        case 2: hipLaunchKernelGGL((decode_gqa_fp8_mfma_kernel<2>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((decode_gqa_fp8_mfma_kernel<4>), grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((decode_gqa_fp8_mfma_kernel<8>), grid, block, 0, st, a); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+}  // namespace pa

@@ -29,11 +29,13 @@ constexpr int kMaxPartition = 1 << 20;
 
 }  // namespace
 
-DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype) {
+DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size) {
     DecodeGeometry g;
+    // fp8 KV is only paired with a bf16 query (checked with the arguments)
+    g.mfma = gqa_mfma_supported(PA_BF16, kv_dtype, head_dim, group_size);
     g.kv_bytes = kv_dtype == PA_FP8_E4M3 ? 1 : 2;
     g.row_lanes = head_dim * g.kv_bytes / 16;
-    g.rows = 64 / g.row_lanes;
+    g.rows = g.mfma ? kDecodeWaves : 64 / g.row_lanes;
     g.elems = 16 / g.kv_bytes;
     return g;
 }
@@ -84,7 +86,7 @@ bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
     if (partition_size != 0 && (partition_size % block_size != 0 || partition_size > kMaxPartition))
         return false;
     DecodePlan p;
-    p.geo = decode_geometry(head_dim, kv_dtype);
+    p.geo = decode_geometry(head_dim, kv_dtype, num_heads / num_kv_heads);
     p.groups = (num_kv_heads + p.geo.rows - 1) / p.geo.rows;
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
     int part = partition_size;

@@ -18,14 +18,20 @@ constexpr int kDecodeWaves = kDecodeThreads / 64;
 // one KV head (head_dim elements) is read by `row_lanes` lanes with one
 // 16-byte load each, so one wave-wide load covers `rows` = 64 / row_lanes
 // consecutive KV heads of one token.  A workgroup owns such a group of heads.
+//
+// Grouped-query attention over fp8 KV with head_dim 128 runs instead on the
+// matrix cores (decode_gqa_mfma.hip): one wave per KV head, 4 KV heads per
+// workgroup.
 struct DecodeGeometry {
+    bool mfma;       // grouped-query fp8 kernel on the matrix cores
     int kv_bytes;    // bytes per KV element
-    int row_lanes;   // lanes per KV-head row
+    int row_lanes;   // lanes per KV-head row (vector kernel)
     int rows;        // KV heads per workgroup
-    int elems;       // KV elements per lane per token (16 / kv_bytes)
+    int elems;       // KV elements per lane per token (vector kernel)
 };
 
-DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype);
+bool gqa_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int group_size);
+DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size);
 
 // Host-side launch plan of one pa_decode call.
 struct DecodePlan {
@@ -77,6 +83,7 @@ struct WriteArgs {
 // Launchers (defined next to their kernels).  Return the hipError_t as int.
 int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype, pa_dtype kv_dtype,
                   int head_dim, int group_size, void* stream);
+int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream);
 int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream);
 
 }  // namespace pa

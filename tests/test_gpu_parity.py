@@ -75,6 +75,9 @@ SMALL_CASES = {
     "gqa2_fp8_d64": ([40, 120, 2], 8, 4, 64, 16, "bf16", "fp8_e4m3"),
     "mha_fp8_d128_partial_group": ([40, 160], 4, 4, 128, 16, "bf16", "fp8_e4m3"),
     "gqa8_fp8_d128": ([40, 160], 16, 2, 128, 16, "bf16", "fp8_e4m3"),
+    "gqa2_fp8_d128_bs32": ([33, 1, 95, 288], 16, 8, 128, 32, "bf16", "fp8_e4m3"),
+    "gqa4_fp8_d128_many_heads": ([17, 48, 500], 64, 16, 128, 16, "bf16", "fp8_e4m3"),
+    "gqa4_fp8_d128_partial_wave_group": ([70, 300], 24, 6, 128, 16, "bf16", "fp8_e4m3"),
 }
 
 
@@ -124,6 +127,42 @@ def test_one_hot_probe_reads_the_addressed_slot(bs):
         got = gpu_decode(b, dev_pool(pool_u, "f16"), q, bt, b.context_lens, partition_size=bs)
         for s, (blk, off) in enumerate(targets):
             assert np.array_equal(got[s], oracle.to_f64(pool_u[blk, 1, off], "f16")), (s, t_rel)
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(32, 8, 16), (32, 8, 32), (8, 8, 16)])
+def test_fp8_one_hot_probe_reads_every_code(hq, hkv, bs):
+    """fp8 KV: the probed token's V row comes out exactly (v_scale 1), which
+    checks the e4m3 decode of all 256 codes in the decode kernels."""
+    lens = [40, 75]
+    b = make_custom(f"probe8_{hq}_{bs}", 15, lens, hq, hkv, 128, bs, "bf16", "fp8_e4m3")
+    bt = b.block_table_array()
+    rng = np.random.default_rng(16)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    pool = rng.choice(finite, size=b.kv_source.shape).astype(np.uint8)
+    pool[:, 0, :, :, 0] = 0                                  # K dim 0 is 0 except at the probe
+    q = np.zeros((len(lens), hq, 128), dtype=np.float32)
+    q[:, :, 0] = 16.0
+    q_bits = (q.view(np.uint32) >> 16).astype(np.uint16)
+    codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    for t_probe in (5, 17):
+        for half in range(2):
+            pl = pool.copy()
+            targets = []
+            for s, L in enumerate(lens):
+                blk, off = b.tables[s][t_probe // bs], t_probe % bs
+                pl[blk, 0, off, :, 0] = 0x62                     # e4m3 40.0
+                pl[blk, 1, off, :, :] = codes[half]
+                targets.append((blk, off))
+            scale = float(np.float32(1 / np.sqrt(128)))
+            qd = dev16(q_bits, "bf16")
+            out = pa.decode(qd, dev_pool(pl, "fp8_e4m3"), dev_i32(bt), dev_i32(b.context_lens), scale, 1.0, 1.0,
+                            partition_size=bs)
+            torch.cuda.synchronize()
+            got = oracle.to_f64(host_bits(out), "bf16")
+            want = oracle.e4m3_decode(codes[half])
+            for s in range(len(lens)):
+                for h in range(hq):
+                    np.testing.assert_array_equal(got[s, h], want)
 
 
 def test_permuting_physical_blocks_is_bit_identical():
