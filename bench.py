@@ -137,19 +137,20 @@ def upload(b, torch, pa, copies: int):
     new_k = d16(b.new_key[0], b.src_dtype)
     new_v = d16(b.new_value[0], b.src_dtype)
     if b.kv_dtype == "fp8_e4m3":
-        # Fill the fp8 pool through the cache write itself, one position at a
-        # time (prefill by repeated decode-step writes) from the generated
-        # pre-quantisation values.
+        # Fill the fp8 pool through the cache write itself, in one launch:
+        # every slot (block b, offset o) is presented as a one-token sequence
+        # whose table is [b] and whose length is o + 1, so the write kernel
+        # quantises each generated value into its own slot.
+        nb, _, bs, hkv, hd = b.kv_source.shape
         src = d16(b.kv_source, b.src_dtype)
-        pool = torch.full(b.kv_source.shape, 0x7F, dtype=torch.uint8, device=dev)
-        L = lens.long()
-        for t in range(int(b.context_lens.max())):
-            blk = bt[:, t // b.block_size].long()
-            off = t % b.block_size
-            lens_t = torch.where(L > t, torch.full_like(lens, t + 1), torch.zeros_like(lens))
-            pa.cache_write(pool, src[blk, 0, off].contiguous(), src[blk, 1, off].contiguous(), bt, lens_t,
-                           b.k_scale, b.v_scale)
+        keys = src[:, 0].reshape(nb * bs, hkv, hd).contiguous()
+        vals = src[:, 1].reshape(nb * bs, hkv, hd).contiguous()
         del src
+        slot_tables = torch.arange(nb, dtype=torch.int32, device=dev).repeat_interleave(bs).reshape(-1, 1)
+        slot_lens = (torch.arange(nb * bs, dtype=torch.int32, device=dev) % bs + 1).contiguous()
+        pool = torch.empty(b.kv_source.shape, dtype=torch.uint8, device=dev)
+        pa.cache_write(pool, keys, vals, slot_tables, slot_lens, b.k_scale, b.v_scale)
+        del keys, vals, slot_tables, slot_lens
     else:
         pool = d16(b.kv_pool, b.kv_dtype)
     pools = [pool] + [pool.clone() for _ in range(copies - 1)]

@@ -13,10 +13,12 @@
 //   or 32), keeping two steps of K/V loads in flight.
 //
 // Per step, per wave (lane l: n = l % 16, q = l / 16):
-//   QK   A = K rows: lane (token n of the half, bytes 32q..32q+31 of the head's
-//        128-byte row), widened fp8 -> bf16 (exact); B = query: lane (head n,
-//        head_dim 32q..32q+31), zero for n >= G.  4 MFMAs per half give
-//        S[token][head] with lane (q, n) holding tokens 4q..4q+3 of head n.
+//   QK   A = K rows: lane (token n of the half, bytes 16q..16q+15 and
+//        64+16q..64+16q+15 of the head's 128-byte row -- each load instruction
+//        then covers whole 64-byte spans), widened fp8 -> bf16 (exact); B =
+//        query: lane (head n, the same 32 head_dim positions), zero for
+//        n >= G.  4 MFMAs per half give S[token][head] with lane (q, n)
+//        holding tokens 4q..4q+3 of head n.
 //   soft running max over the 32 tokens (in-lane, then across the 4 rows),
 //        exp2-domain probabilities; masked tokens get weight 0.
 //   PV   A = P: exactly the lane's own 8 probabilities (k-slot 8q+j is token
@@ -111,10 +113,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     // ---- query operand: head n of this KV head's group, head_dim 32q.. ----
     bf16x8 qop[4];
     {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.query) + ((int64_t)s * Hq + g * G + (n < G ? n : 0)) * kD + 32 * q;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.query) + ((int64_t)s * Hq + g * G + (n < G ? n : 0)) * kD + 16 * q;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint4 v = n < G ? *reinterpret_cast<const uint4*>(qp + 8 * c) : make_uint4(0, 0, 0, 0);
+            const int d0 = (c >> 1) * 64 + (c & 1) * 8;
+            const uint4 v = n < G ? *reinterpret_cast<const uint4*>(qp + d0) : make_uint4(0, 0, 0, 0);
             qop[c] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     const int shift = a.block_shift;
     const uint32_t row_bytes = (uint32_t)(a.num_kv_heads * kD);               // fp8: 1 byte per element
     const uint32_t half_bytes = row_bytes << shift;                           // K half -> V half
-    const uint32_t lane_col = (uint32_t)(g * kD + 32 * q);                    // this lane's 32 bytes of a row
+    const uint32_t lane_col = (uint32_t)(g * kD + 16 * q);                    // bytes 16q.. and 64+16q.. of the head's row
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
     const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
@@ -163,9 +166,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
                 const int64_t row = ((int64_t)(ok ? blk : 0) * 2 << shift) + (tok & (a.block_size - 1));
                 const uint8_t* kp = pool + row * row_bytes + lane_col;
                 kr[2 * u] = stream_load(kp);
-                kr[2 * u + 1] = stream_load(kp + 16);
+                kr[2 * u + 1] = stream_load(kp + 64);
                 vr[2 * u] = stream_load(kp + half_bytes);
-                vr[2 * u + 1] = stream_load(kp + half_bytes + 16);
+                vr[2 * u + 1] = stream_load(kp + half_bytes + 64);
             }
         };
 
@@ -183,9 +186,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
             // stage V rows (row 16u + n) for the transposed reads below
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                uint8_t* dst = sv + (16 * u + n) * kRowStride + 32 * q;
+                uint8_t* dst = sv + (16 * u + n) * kRowStride + 16 * q;
                 *reinterpret_cast<uint4*>(dst) = vr[2 * u];
-                *reinterpret_cast<uint4*>(dst + 16) = vr[2 * u + 1];
+                *reinterpret_cast<uint4*>(dst + 64) = vr[2 * u + 1];
             }
             // QK: S[token][head] for both halves
             f32x4 sacc[2];

@@ -92,3 +92,35 @@ def assert_decode_close(got, ref, batch, seqs=None):
     worst = float((err - bound).max()) if err.size else 0.0
     assert worst <= 0, f"max abs err {err.max():.3e} (tolerance {tol:g})"
     return float(err.max()) if err.size else 0.0
+
+
+def gpu_fp8_pool_from_source(batch) -> torch.Tensor:
+    """fp8 pool built on the GPU by the cache write itself, in one launch:
+    every slot (block b, offset o) is written as a one-token sequence whose
+    table is [b] and whose length is o + 1."""
+    nb, _, bs, hkv, hd = batch.kv_source.shape
+    src = dev16(batch.kv_source, batch.src_dtype)
+    keys = src[:, 0].reshape(nb * bs, hkv, hd).contiguous()
+    vals = src[:, 1].reshape(nb * bs, hkv, hd).contiguous()
+    del src
+    tables = torch.arange(nb, dtype=torch.int32, device="cuda").repeat_interleave(bs).reshape(-1, 1)
+    lens = (torch.arange(nb * bs, dtype=torch.int32, device="cuda") % bs + 1).contiguous()
+    pool = torch.empty(batch.kv_source.shape, dtype=torch.uint8, device="cuda")
+    pa.cache_write(pool, keys, vals, tables, lens, batch.k_scale, batch.v_scale)
+    torch.cuda.synchronize()
+    return pool
+
+
+def oracle_decode_sampled(batch, pool_raw, query_raw, bt, lens, seqs):
+    """Oracle output rows for a few sequences, encoding (fp8) or copying only
+    the blocks those sequences read."""
+    out = np.zeros((batch.num_seqs, batch.num_heads, batch.head_dim))
+    for s in seqs:
+        blocks = sorted(set(int(x) for x in batch.tables[s]))
+        remap = {blk: i for i, blk in enumerate(blocks)}
+        sub = pool_raw(blocks)
+        bt_s = np.array([[remap[int(x)] for x in batch.tables[s]]], dtype=np.int32)
+        out[s] = oracle.paged_decode(query_raw[s:s + 1], batch.q_dtype, sub, batch.kv_dtype, bt_s,
+                                     lens[s:s + 1], batch.block_size, batch.scale, batch.k_scale,
+                                     batch.v_scale)[0]
+    return out
