@@ -40,6 +40,7 @@
 
 #include <stdint.h>
 
+#include "decode_common.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -172,16 +173,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     __shared__ float s_o[NW][64 * EPL];
 
     // ---- which (sequence, KV-head group, partition) -------------------------
-    const int wg = blockIdx.x;
-    const int group = wg % a.groups;
-    const int rest = wg / a.groups;
-    const int s = rest % a.num_seqs;
-    const int p = rest / a.num_seqs;
-
-    const int max_tokens = a.max_blocks_per_seq << a.block_shift;
-    const int L = min(a.context_lens[s], max_tokens);
-    const int n_part = L > 0 ? (L + a.partition - 1) / a.partition : 0;
-    if (p >= (n_part > 0 ? n_part : 1)) return;
+    WorkItem w;
+    if (!find_work(a, blockIdx.x, w)) return;
+    const int s = w.s, p = w.p, group = w.group, L = w.L, n_part = w.n_part;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;

@@ -10,7 +10,8 @@
 //   head 4*group + w for the whole partition, so the waves never exchange
 //   softmax state.  A wave walks its partition in steps of 32 tokens (two
 //   16-token halves; a half never crosses a block boundary for block size 16
-//   or 32), keeping two steps of K/V loads in flight.
+//   or 32), keeping kGqaStages steps of K/V loads in flight (at two waves
+//   per SIMD the in-flight bytes, not the ALUs, set the rate).
 //
 // Per step, per wave (lane l: n = l % 16, q = l / 16):
 //   QK   A = K rows: lane (token n of the half, bytes 16q..16q+15 and
@@ -34,6 +35,7 @@
 
 #include <stdint.h>
 
+#include "decode_common.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -48,6 +50,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 constexpr int kD = 128;                  // head_dim
 constexpr int kRowStride = 144;          // LDS bytes per staged V row (128 + 16 against bank conflicts)
 constexpr int kStepTokens = 32;
+constexpr int kGqaStages = 2;            // 32-token steps of K/V loads each wave keeps in flight
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -85,15 +88,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     constexpr int NW = kDecodeWaves;
     __shared__ __attribute__((aligned(16))) uint8_t s_v[NW][kStepTokens * kRowStride];
 
-    const int wg = blockIdx.x;
-    const int group = wg % a.groups;
-    const int rest = wg / a.groups;
-    const int s = rest % a.num_seqs;
-    const int p = rest / a.num_seqs;
-    const int max_tokens = a.max_blocks_per_seq << a.block_shift;
-    const int L = min(a.context_lens[s], max_tokens);
-    const int n_part = L > 0 ? (L + a.partition - 1) / a.partition : 0;
-    if (p >= (n_part > 0 ? n_part : 1)) return;
+    // ---- which (sequence, KV-head group, partition) -------------------------
+    WorkItem w;
+    if (!find_work(a, blockIdx.x, w)) return;
+    const int s = w.s, p = w.p, group = w.group, L = w.L, n_part = w.n_part;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -255,13 +253,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
             }
         };
 
-        uint4 ka[4], va[4], kb[4], vb[4];
-        issue(0, ka, va);
-        for (int k = 0; k < n_steps; k += 2) {
-            issue(k + 1, kb, vb);
-            compute(k, ka, va);
-            issue(k + 2, ka, va);
-            compute(k + 1, kb, vb);
+        constexpr int NS = kGqaStages;
+        uint4 kr[NS][4], vr[NS][4];
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st) issue(st, kr[st], vr[st]);
+        for (int k = 0; k < n_steps; k += NS) {
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const int nxt = (st + NS - 1) % NS;
+                issue(k + st + NS - 1, kr[nxt], vr[nxt]);
+                compute(k + st, kr[st], vr[st]);
+            }
         }
     }
 

@@ -91,11 +91,11 @@ bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
     int part = partition_size;
     if (part == 0) {
-        // Enough workgroups to fill 256 CUs several times over when every
-        // sequence is at its longest, without splitting sequences into
-        // slivers whose partial results cost more than they save.
+        // The largest partition (fewest partials, least per-workgroup start-up)
+        // that still gives at least 2048 workgroups -- 256 CUs several times
+        // over -- when every sequence is at its longest.
         const int64_t heads_x_seqs = (int64_t)p.groups * num_seqs;
-        part = 512;
+        part = 1024;
         while (part > 64 && heads_x_seqs * ((max_tokens + part - 1) / part) < 2048) part /= 2;
         if (part < block_size) part = block_size;
         part = (part + block_size - 1) / block_size * block_size;
