@@ -8,9 +8,10 @@ from the 256 MB last-level cache.
 
 Prints one JSON line:
   value       KV-read GB/s of the whole step (algorithmic bytes / step time)
-  roofline    the decode kernel's algorithmic bytes / its mean duration from
-              HIP events recorded around every launch in the timed region,
-              against the 8 TB/s HBM peak
+  roofline    the attention kernel's (pa_decode_partials) algorithmic bytes /
+              its mean duration from HIP events recorded around every launch
+              in the timed region, against the 8 TB/s HBM peak; the whole
+              pa_decode call (attention + split-K merge) is reported beside it
   cpu_baseline  the float64 CPU oracle on the same batch (1 BLAS thread)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama7b]
@@ -71,7 +72,7 @@ def counter_traffic(config: str, partition: int):
         rec = json.load(f)
     if rec.get("source_hash") != source_hash() or rec.get("partition") != partition:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("attention_hbm_bytes_per_launch")
 
 
 def stream_read_gbs(torch, nbytes: int = 4 << 30, reps: int = 10) -> float:
@@ -257,22 +258,28 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
+        # one pass of the hot path: cache write, attention pass, split-K merge
+        # (pa_decode == pa_decode_partials + pa_decode_merge, timed apart)
         pool = dev["pools"][i % copies]
+        dargs = (dev["q"], pool, dev["bt"], dev["lens"], b.scale, b.k_scale, b.v_scale)
+        dkw = dict(out=out, workspace=ws, partition_size=args.partition_size)
         if ev is not None:
             ev[0].record(stream)
         pa.cache_write(pool, dev["k"], dev["v"], dev["bt"], dev["lens"], b.k_scale, b.v_scale)
         if ev is not None:
             ev[1].record(stream)
-        pa.decode(dev["q"], pool, dev["bt"], dev["lens"], b.scale, b.k_scale, b.v_scale, out=out,
-                  workspace=ws, partition_size=args.partition_size)
+        pa.decode(*dargs, phase="partials", **dkw)
         if ev is not None:
             ev[2].record(stream)
+        pa.decode(*dargs, phase="merge", **dkw)
+        if ev is not None:
+            ev[3].record(stream)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -281,15 +288,18 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     write_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    merge_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    call_ms = np.array([e[1].elapsed_time(e[3]) for e in events])
     ms_step = wall * 1e3 / args.steps
-    dec_us = float(decode_ms.mean() * 1e3)
-    achieved = nbytes["decode"] / (dec_us * 1e-6) / 1e9
+    attn_us = float(attn_ms.mean() * 1e3)
+    call_us = float(call_ms.mean() * 1e3)
+    achieved = nbytes["decode"] / (attn_us * 1e-6) / 1e9
     step_bytes = nbytes["decode"] + nbytes["write"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"decode mean {dec_us:.1f} us (p10 {np.percentile(decode_ms, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(decode_ms, 90) * 1e3:.1f}); write mean {write_ms.mean() * 1e3:.1f} us; "
-        f"step {ms_step * 1e3:.1f} us")
+    log(f"attention pass mean {attn_us:.1f} us (p10 {np.percentile(attn_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(attn_ms, 90) * 1e3:.1f}); merge {merge_ms.mean() * 1e3:.1f} us; "
+        f"pa_decode call {call_us:.1f} us; write {write_ms.mean() * 1e3:.1f} us; step {ms_step * 1e3:.1f} us")
     traffic = counter_traffic(args.config, partition)
     achievable = stream_read_gbs(torch)
     log(f"streaming-read kernel reaches {achievable:.0f} GB/s on this device")
@@ -315,7 +325,10 @@ def main() -> int:
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s_per_layer": round(b.num_seqs / (ms_step * 1e-3), 1),
-        "decode_kernel_us": round(dec_us, 2),
+        "decode_attention_kernel_us": round(attn_us, 2),
+        "decode_merge_kernel_us": round(float(merge_ms.mean() * 1e3), 2),
+        "decode_call_us": round(call_us, 2),
+        "decode_call_gbs": round(nbytes["decode"] / (call_us * 1e-6) / 1e9, 1),
         "hbm_read_achievable_gbs": round(achievable, 1),
         "decode_frac_of_achievable": round(achieved / achievable, 4),
         "write_kernel_us": round(float(write_ms.mean() * 1e3), 2),
@@ -330,7 +343,7 @@ def main() -> int:
         "algorithmic_bytes": nbytes,
     }
     if b.notes.get("prefix_blocks"):
-        res["unique_kv_gbs"] = round(nbytes["unique_kv_blocks"] / (dec_us * 1e-6) / 1e9, 1)
+        res["unique_kv_gbs"] = round(nbytes["unique_kv_blocks"] / (attn_us * 1e-6) / 1e9, 1)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)

@@ -167,6 +167,35 @@ pa_status pa_decode(void* out, const void* query, pa_dtype q_dtype,
                     float scale, float k_scale, float v_scale, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_partials, pa_decode_merge -- the two launches pa_decode makes, for
+ * callers that want to schedule or time them separately.  Arguments and
+ * checks are exactly those of pa_decode.  pa_decode_partials runs the
+ * attention pass: it writes the final output of every sequence that fits in
+ * one partition and leaves per-partition partial softmax states (running
+ * max, sum, unnormalised output) in the workspace for the others.
+ * pa_decode_merge, enqueued after it on the same stream with the same
+ * arguments and workspace, combines those partials into the output of the
+ * split sequences (split-K merge); it enqueues nothing when no sequence can
+ * be split.  pa_decode == pa_decode_partials followed by pa_decode_merge.
+ */
+pa_status pa_decode_partials(void* out, const void* query, pa_dtype q_dtype,
+                             const void* kv_pool, pa_dtype kv_dtype,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int32_t num_blocks, float scale, float k_scale, float v_scale,
+                             int32_t partition_size, void* workspace, size_t workspace_bytes,
+                             void* stream);
+pa_status pa_decode_merge(void* out, const void* query, pa_dtype q_dtype,
+                          const void* kv_pool, pa_dtype kv_dtype,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int32_t num_blocks, float scale, float k_scale, float v_scale,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Human-readable name of a status value (static storage, never NULL). */
 const char* pa_status_string(pa_status status);
 

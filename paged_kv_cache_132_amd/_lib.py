@@ -20,8 +20,8 @@ STATUS_NAMES = {
     0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
     4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_MISALIGNED", 6: "PA_ERR_WORKSPACE_TOO_SMALL", 7: "PA_ERR_HIP",
 }
-EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_decode_partition_size",
-            "pa_status_string")
+EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_partials", "pa_decode_merge",
+            "pa_decode_workspace_size", "pa_decode_partition_size", "pa_status_string")
 
 _lib = None
 _lock = threading.Lock()
@@ -40,10 +40,10 @@ def load() -> ctypes.CDLL:
         lib.pa_cache_write.restype = ctypes.c_int
         lib.pa_cache_write.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp,
                                        i32, i32, i32, i32, i32, i32, f32, f32, vp]
-        lib.pa_decode.restype = ctypes.c_int
-        lib.pa_decode.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
-                                  i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
-                                  vp, sz, vp]
+        for fn in (lib.pa_decode, lib.pa_decode_partials, lib.pa_decode_merge):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                           i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, vp, sz, vp]
         lib.pa_decode_workspace_size.restype = sz
         lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
         lib.pa_decode_partition_size.restype = i32
@@ -151,8 +151,11 @@ _default_ws: dict = {}
 def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tensor,
            context_lens: torch.Tensor, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
            out: torch.Tensor | None = None, workspace: torch.Tensor | Workspace | None = None,
-           partition_size: int = 0, stream=None) -> torch.Tensor:
-    """Paged decode attention; returns out [num_seqs, num_heads, head_dim] of query's dtype."""
+           partition_size: int = 0, stream=None, phase: str = "both") -> torch.Tensor:
+    """Paged decode attention; returns out [num_seqs, num_heads, head_dim] of query's dtype.
+
+    phase: "both" (pa_decode), "partials" (pa_decode_partials) or "merge"
+    (pa_decode_merge, with the same arguments and workspace as the partials call)."""
     nb, bs, hkv, d = _pool_dims(kv_pool)
     if query.dim() != 3 or query.shape[2] != d or not query.is_contiguous():
         raise ValueError("query must be a contiguous [num_seqs, num_heads, head_dim] tensor")
@@ -170,9 +173,10 @@ def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tenso
         ws = workspace.get(need, query.device)
     else:
         ws = workspace
-    st = load().pa_decode(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), kvt,
+    fn = {"both": load().pa_decode, "partials": load().pa_decode_partials, "merge": load().pa_decode_merge}[phase]
+    st = fn(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), kvt,
                           _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, mb, nb,
                           float(scale), float(k_scale), float(v_scale), int(partition_size),
                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "pa_decode")
+    _check(st, f"pa_decode ({phase})")
     return out

@@ -459,15 +459,17 @@ int launch_t(const DecodeArgs& a, const DecodePlan& plan, int head_dim, int grou
 }  // namespace
 
 int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype, pa_dtype kv_dtype,
-                  int head_dim, int group_size, void* stream) {
+                  int head_dim, int group_size, int phases, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (plan.grid == 0) return 0;
-    int err;
-    if (plan.geo.mfma) err = launch_decode_gqa_mfma(a, plan, group_size, stream);
-    else if (kv_dtype == PA_F16) err = launch_t<PA_F16, PA_F16>(a, plan, head_dim, group_size, st);
-    else if (kv_dtype == PA_BF16) err = launch_t<PA_BF16, PA_BF16>(a, plan, head_dim, group_size, st);
-    else err = launch_t<PA_BF16, PA_FP8_E4M3>(a, plan, head_dim, group_size, st);
-    if (err != 0 || plan.max_partitions <= 1) return err;
+    int err = 0;
+    if (phases & kPhasePartials) {
+        if (plan.geo.mfma) err = launch_decode_gqa_mfma(a, plan, group_size, stream);
+        else if (kv_dtype == PA_F16) err = launch_t<PA_F16, PA_F16>(a, plan, head_dim, group_size, st);
+        else if (kv_dtype == PA_BF16) err = launch_t<PA_BF16, PA_BF16>(a, plan, head_dim, group_size, st);
+        else err = launch_t<PA_BF16, PA_FP8_E4M3>(a, plan, head_dim, group_size, st);
+    }
+    if (err != 0 || !(phases & kPhaseMerge) || plan.max_partitions <= 1) return err;
     const bool f16 = q_dtype == PA_F16;
     if (head_dim == 64) return f16 ? launch_merge<PA_F16, 64>(a, st) : launch_merge<PA_BF16, 64>(a, st);
     return f16 ? launch_merge<PA_F16, 128>(a, st) : launch_merge<PA_BF16, 128>(a, st);

@@ -194,7 +194,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
     return p.bytes;
 }
 
-pa_status pa_decode(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
+static pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
                     pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
@@ -237,8 +237,23 @@ pa_status pa_decode(void* out, const void* query, pa_dtype q_dtype, const void* 
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;
     const int err = launch_decode(a, plan, q_dtype, kv_dtype, head_dim, num_heads / num_kv_heads,
-                                  stream);
+                                  phases, stream);
     return err == 0 ? PA_OK : PA_ERR_HIP;
 }
+
+#define PA_DECODE_PARAMS                                                                          \
+    void *out, const void *query, pa_dtype q_dtype, const void *kv_pool, pa_dtype kv_dtype,       \
+        const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,               \
+        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,            \
+        int32_t max_blocks_per_seq, int32_t num_blocks, float scale, float k_scale, float v_scale, \
+        int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream
+#define PA_DECODE_ARGS                                                                              \
+    out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens, num_seqs, num_heads,        \
+        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, \
+        partition_size, workspace, workspace_bytes, stream
+
+pa_status pa_decode(PA_DECODE_PARAMS) { return decode_phases(kPhasePartials | kPhaseMerge, PA_DECODE_ARGS); }
+pa_status pa_decode_partials(PA_DECODE_PARAMS) { return decode_phases(kPhasePartials, PA_DECODE_ARGS); }
+pa_status pa_decode_merge(PA_DECODE_PARAMS) { return decode_phases(kPhaseMerge, PA_DECODE_ARGS); }
 
 }  // extern "C"

@@ -81,8 +81,11 @@ struct WriteArgs {
 };
 
 // Launchers (defined next to their kernels).  Return the hipError_t as int.
+// phase bit 1: attention pass (partials), bit 2: split-K merge.
+constexpr int kPhasePartials = 1;
+constexpr int kPhaseMerge = 2;
 int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype, pa_dtype kv_dtype,
-                  int head_dim, int group_size, void* stream);
+                  int head_dim, int group_size, int phases, void* stream);
 int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream);
 int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream);
 

@@ -183,6 +183,25 @@ def test_permuting_physical_blocks_is_bit_identical():
     assert np.array_equal(got, ref)
 
 
+def test_two_phase_calls_equal_pa_decode():
+    """pa_decode_partials followed by pa_decode_merge is pa_decode, bit for bit."""
+    for kvd, qd, hq, hkv in (("f16", "f16", 32, 32), ("fp8_e4m3", "bf16", 32, 8)):
+        b = make_custom("phases", 18, [5, 300, 1000, 64], hq, hkv, 128, 16, qd, kvd)
+        bt, lens = dev_i32(b.block_table_array()), dev_i32(b.context_lens)
+        pool = dev_pool(pool_of(b), kvd)
+        q = dev16(b.query, qd)
+        one = pa.decode(q, pool, bt, lens, b.scale, b.k_scale, b.v_scale, partition_size=64)
+        ws = torch.empty(pa.decode_workspace_size(4, hq, hkv, 128, 16, b.max_blocks_per_seq,
+                                                  pa.pa_dtype(pool), 64), dtype=torch.uint8, device="cuda")
+        two = torch.full_like(one, float("nan"))
+        pa.decode(q, pool, bt, lens, b.scale, b.k_scale, b.v_scale, out=two, workspace=ws, partition_size=64,
+                  phase="partials")
+        pa.decode(q, pool, bt, lens, b.scale, b.k_scale, b.v_scale, out=two, workspace=ws, partition_size=64,
+                  phase="merge")
+        torch.cuda.synchronize()
+        assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
 def test_workspace_contents_do_not_matter():
     """The workspace is scratch: garbage on entry, or reuse across calls of
     other sizes, changes nothing."""
