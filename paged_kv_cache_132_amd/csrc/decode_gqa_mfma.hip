@@ -14,12 +14,16 @@
 //   per SIMD the in-flight bytes, not the ALUs, set the rate).
 //
 // Per step, per wave (lane l: n = l % 16, q = l / 16):
-//   QK   A = K rows: lane (token n of the half, bytes 16q..16q+15 and
-//        64+16q..64+16q+15 of the head's 128-byte row -- each load instruction
-//        then covers whole 64-byte spans), widened fp8 -> bf16 (exact); B =
-//        query: lane (head n, the same 32 head_dim positions), zero for
-//        n >= G.  4 MFMAs per half give S[token][head] with lane (q, n)
-//        holding tokens 4q..4q+3 of head n.
+//   load each load instruction reads 8 whole 128-byte head rows (8 lanes x
+//        16 bytes per token); the rows are staged in this wave's LDS and read
+//        back in operand layout.  (Operand-layout loads -- 16 tokens x 64
+//        bytes per instruction -- reached only ~3.9 TB/s even with no
+//        arithmetic at all; whole-row loads ~5.4 TB/s.)
+//   QK   A = K rows: lane (token n of the half, head_dim 16q..16q+15 and
+//        64+16q..64+16q+15), widened fp8 -> bf16 (exact); B = query: lane
+//        (head n, the same 32 head_dim positions), zero for n >= G.  4 MFMAs
+//        per half give S[token][head] with lane (q, n) holding tokens
+//        4q..4q+3 of head n.
 //   soft running max over the 32 tokens (in-lane, then across the 4 rows),
 //        exp2-domain probabilities; masked tokens get weight 0.
 //   PV   A = P: exactly the lane's own 8 probabilities (k-slot 8q+j is token
@@ -86,7 +90,7 @@ template <int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(DecodeArgs a) {
     static_assert(G == 2 || G == 4 || G == 8, "query heads per KV head");
     constexpr int NW = kDecodeWaves;
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[NW][kStepTokens * kRowStride];
+    __shared__ __attribute__((aligned(16))) uint8_t s_kv[NW][2][kStepTokens * kRowStride];
 
     // ---- which (sequence, KV-head group, partition) -------------------------
     WorkItem w;
@@ -125,12 +129,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     const int shift = a.block_shift;
     const uint32_t row_bytes = (uint32_t)(a.num_kv_heads * kD);               // fp8: 1 byte per element
     const uint32_t half_bytes = row_bytes << shift;                           // K half -> V half
-    const uint32_t lane_col = (uint32_t)(g * kD + 16 * q);                    // bytes 16q.. and 64+16q.. of the head's row
+    const uint32_t lane_col = (uint32_t)(g * kD + 16 * (lane & 7));           // 16-byte chunk of the head's row
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
     const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
-    // LDS: this wave's V staging rows; transposed-read base address of this lane
-    uint8_t* sv = s_v[wave];
+    // LDS: this wave's K and V staging rows; transposed-read base address of this lane
+    uint8_t* sk = s_kv[wave][0];
+    uint8_t* sv = s_kv[wave][1];
     const int jj = n >> 1;
     const uint32_t tr_off = (uint32_t)((16 * (jj >> 2) + 4 * q + (jj & 3)) * kRowStride + 8 * (lane & 1));
 
@@ -149,9 +154,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
         const int seg_t1 = min(t_end, (seg0 + seg_blocks) << shift);
         const int n_steps = (seg_t1 - seg_t0 + kStepTokens - 1) / kStepTokens;
 
-        // Issue the K and V loads of step k (two halves x 32 bytes per lane).
-        // Rows past the end are redirected to the first row of the step, which
-        // is always valid, and are masked out of the softmax.
+        // Issue the K and V loads of step k.  Each load instruction reads 8
+        // whole 128-byte head rows (8 lanes x 16 bytes per token): long runs
+        // keep the request count per byte low.  Rows past the end are
+        // redirected to the first row of their half, which is always valid,
+        // and are masked out of the softmax.
         auto issue = [&](int k, uint4 (&kr)[4], uint4 (&vr)[4]) {
             const int kk = min(k, n_steps - 1);
             const int t0 = seg_t0 + kk * kStepTokens;
@@ -160,13 +167,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
                 const int th = min(t0 + 16 * u, seg_t1 - 1) & ~15;       // half start (clamped into range)
                 const int blk = __builtin_amdgcn_readlane(my_blk, (th >> shift) - seg0);
                 const bool ok = blk >= 0 && blk < a.num_blocks;
-                const int tok = (th + n < seg_t1) ? th + n : th;
-                const int64_t row = ((int64_t)(ok ? blk : 0) * 2 << shift) + (tok & (a.block_size - 1));
-                const uint8_t* kp = pool + row * row_bytes + lane_col;
-                kr[2 * u] = stream_load(kp);
-                kr[2 * u + 1] = stream_load(kp + 64);
-                vr[2 * u] = stream_load(kp + half_bytes);
-                vr[2 * u + 1] = stream_load(kp + half_bytes + 64);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = th + 8 * j + (lane >> 3);
+                    const int tok = t < seg_t1 ? t : th;
+                    const int64_t row = ((int64_t)(ok ? blk : 0) * 2 << shift) + (tok & (a.block_size - 1));
+                    const uint8_t* kp = pool + row * row_bytes + lane_col;
+                    kr[2 * u + j] = stream_load(kp);
+                    vr[2 * u + j] = stream_load(kp + half_bytes);
+                }
             }
         };
 
@@ -181,20 +190,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
                 const int blk = th < seg_t1 ? __builtin_amdgcn_readlane(my_blk, (th >> shift) - seg0) : -1;
                 half_ok[u] = th < seg_t1 && blk >= 0 && blk < a.num_blocks;
             }
-            // stage V rows (row 16u + n) for the transposed reads below
+            // stage the step's K and V rows (row 16u + 8j + lane/8, chunk lane%8)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                uint8_t* dst = sv + (16 * u + n) * kRowStride + 16 * q;
-                *reinterpret_cast<uint4*>(dst) = vr[2 * u];
-                *reinterpret_cast<uint4*>(dst + 64) = vr[2 * u + 1];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t off = (uint32_t)((16 * u + 8 * j + (lane >> 3)) * kRowStride + 16 * (lane & 7));
+                    *reinterpret_cast<uint4*>(sk + off) = kr[2 * u + j];
+                    *reinterpret_cast<uint4*>(sv + off) = vr[2 * u + j];
+                }
             }
-            // QK: S[token][head] for both halves
+            // QK: S[token][head] for both halves; A operand of lane (token n,
+            // k-group q) = head_dim 16q..16q+15 and 64+16q..64+16q+15
             f32x4 sacc[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
+                const uint8_t* rowp = sk + (16 * u + n) * kRowStride + 16 * q;
+                const uint4 lo = *reinterpret_cast<const uint4*>(rowp);
+                const uint4 hi = *reinterpret_cast<const uint4*>(rowp + 64);
+                const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const uint32_t w[8] = {kr[2 * u].x, kr[2 * u].y, kr[2 * u].z, kr[2 * u].w,
-                                       kr[2 * u + 1].x, kr[2 * u + 1].y, kr[2 * u + 1].z, kr[2 * u + 1].w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w[2 * c], w[2 * c + 1]), qop[c], acc, 0, 0, 0);
