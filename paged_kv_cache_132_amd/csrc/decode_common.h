@@ -48,13 +48,14 @@ __device__ __forceinline__ int wave_total(int v) {
 // sequence is the (k - C(p))-th sequence, in order, with items(s) > p.
 // Each wave computes this on its own -- no LDS, no barriers -- so waves of a
 // workgroup may call it independently; they all reach the same answer.
+constexpr int kXcds = 8;                          // accelerator complex dies of the chip
+
 __device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
     constexpr int kCached = 8;                    // sequences 0..511 keep their count in registers
     const int lane = threadIdx.x & 63;
     const int B = a.num_seqs;
     const int P = a.max_partitions;
     const int max_tokens = a.max_blocks_per_seq << a.block_shift;
-    const int k = wg / a.groups;                  // item index ignoring the group
     auto items_of = [&](int s) {
         const int L = min(a.context_lens[s], max_tokens);
         return L > 0 ? (L + a.partition - 1) / a.partition : 1;
@@ -73,7 +74,16 @@ __device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
         for (int s = lane + 64 * kCached; s < B; s += 64) acc += min(items_of(s), p);
         return wave_total(acc);
     };
-    if (k >= C(P)) return false;                  // past the last item
+    // Live items are workgroups 0 .. total-1.  The hardware deals workgroup
+    // ids round-robin to the XCDs (id % kXcds); renumber so that each XCD
+    // takes a contiguous run of items: the KV-head groups of one (sequence,
+    // partition) and neighbouring sequences then share that XCD's L2.
+    const int total = C(P) * a.groups;
+    if (wg >= total) return false;                // past the last item
+    const int x = wg % kXcds, j = wg / kXcds;
+    const int per = total / kXcds, rem = total % kXcds;
+    const int item = x * per + min(x, rem) + j;
+    const int k = item / a.groups;                // item index ignoring the group
     int lo = 0, hi = P;                           // C(lo) <= k < C(hi)
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -100,7 +110,7 @@ __device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
     if (s_found < 0) return false;
     w.s = s_found;
     w.p = p;
-    w.group = wg % a.groups;
+    w.group = item % a.groups;
     w.L = min(a.context_lens[s_found], max_tokens);
     w.n_part = w.L > 0 ? (w.L + a.partition - 1) / a.partition : 0;
     return true;
