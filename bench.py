@@ -6,8 +6,14 @@ The KV pool is replicated R times (at least 2 GiB in all) and successive steps
 rotate through the copies, so each step reads its pool from HBM rather than
 from the 256 MB last-level cache.
 
+Steps run twice: eagerly, with HIP events around every launch (the per-kernel
+breakdown), and as replays of a HIP graph holding the same three launches
+(the step time a decode loop sees once launch gaps are gone).  Each graph's
+output is checked against the eager output before timing.
+
 Prints one JSON line:
-  value       KV-read GB/s of the whole step (algorithmic bytes / step time)
+  value       KV-read GB/s of the whole step (algorithmic bytes / graph-replayed
+              step time; the eager step time is reported beside it)
   roofline    the attention kernel's (pa_decode_partials) algorithmic bytes /
               its mean duration from HIP events recorded around every launch
               in the timed region, against the 8 TB/s HBM peak; the whole
@@ -223,6 +229,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB copy kernel --steps times (HBM counter calibration)")
     args = ap.parse_args()
@@ -287,11 +295,48 @@ def main() -> int:
         step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    eager_ms_step = wall * 1e3 / args.steps
+
+    graph_ms_step = None
+    if not args.eager:
+        # one graph per pool copy, each holding write + attention + merge
+        ref = out.clone()
+        step(args.warmup + args.steps - 1)
+        torch.cuda.synchronize()
+        ref.copy_(out)
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(c)
+                graphs.append(g)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for c, g in enumerate(graphs):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref):
+                raise RuntimeError(f"graph replay {c} differs from the eager step")
+        log(f"graph replay: {copies} graphs checked against the eager step")
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[(args.warmup + i) % copies].replay()
+        torch.cuda.synchronize()
+        graph_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graphs
+
     write_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     attn_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     merge_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
     call_ms = np.array([e[1].elapsed_time(e[3]) for e in events])
-    ms_step = wall * 1e3 / args.steps
+    ms_step = graph_ms_step if graph_ms_step is not None else eager_ms_step
     attn_us = float(attn_ms.mean() * 1e3)
     call_us = float(call_ms.mean() * 1e3)
     achieved = nbytes["decode"] / (attn_us * 1e-6) / 1e9
@@ -299,7 +344,9 @@ def main() -> int:
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"attention pass mean {attn_us:.1f} us (p10 {np.percentile(attn_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(attn_ms, 90) * 1e3:.1f}); merge {merge_ms.mean() * 1e3:.1f} us; "
-        f"pa_decode call {call_us:.1f} us; write {write_ms.mean() * 1e3:.1f} us; step {ms_step * 1e3:.1f} us")
+        f"pa_decode call {call_us:.1f} us; write {write_ms.mean() * 1e3:.1f} us; eager step "
+        f"{eager_ms_step * 1e3:.1f} us; graph step "
+        f"{'-' if graph_ms_step is None else f'{graph_ms_step * 1e3:.1f}'} us")
     traffic = counter_traffic(args.config, partition)
     achievable = stream_read_gbs(torch)
     log(f"streaming-read kernel reaches {achievable:.0f} GB/s on this device")
@@ -324,8 +371,13 @@ def main() -> int:
             "seed": b.seed, "partition_size": partition, "pool_copies": copies,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "step_launch": "hip_graph" if graph_ms_step is not None else "eager",
+        "eager_ms_per_step": round(eager_ms_step, 4),
         "decode_tokens_per_s_per_layer": round(b.num_seqs / (ms_step * 1e-3), 1),
+        "decode_only_tokens_per_s_per_layer": round(b.num_seqs / (call_us * 1e-6), 1),
         "decode_attention_kernel_us": round(attn_us, 2),
+        "decode_attention_kernel_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2)
+                                                   for q in (10, 50, 90)],
         "decode_merge_kernel_us": round(float(merge_ms.mean() * 1e3), 2),
         "decode_call_us": round(call_us, 2),
         "decode_call_gbs": round(nbytes["decode"] / (call_us * 1e-6) / 1e9, 1),

@@ -202,6 +202,58 @@ def test_two_phase_calls_equal_pa_decode():
         assert torch.equal(one.view(torch.int16), two.view(torch.int16))
 
 
+def test_graph_replays_match_eager_and_oracle():
+    """A HIP graph holding cache write + both decode launches gives, on every
+    replay, exactly the eager result (eager work and synchronisations run
+    between the replays), and that result matches the oracle."""
+    for kvd, qd, hq, hkv in (("f16", "f16", 16, 16), ("fp8_e4m3", "bf16", 32, 8)):
+        b = make_custom("graph", 19, [40, 300, 17, 1000], hq, hkv, 128, 16, qd, kvd, appends=1)
+        lens1 = b.context_lens + 1
+        for tab, L in zip(b.tables, lens1):
+            b.manager.grow_to(tab, int(L))
+        bt_np = b.block_table_array()
+        pool_np = pool_of(b)
+        bt, lens = dev_i32(bt_np), dev_i32(lens1)
+        src = "bf16" if kvd == "fp8_e4m3" else kvd
+        k, v = dev16(b.new_key[0], src), dev16(b.new_value[0], src)
+        q = dev16(b.step_query[0], qd)
+        pool = dev_pool(pool_np, kvd)
+        ws = torch.empty(pa.decode_workspace_size(4, hq, hkv, 128, 16, b.max_blocks_per_seq,
+                                                  pa.pa_dtype(pool), 64), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+
+        def step():
+            pa.cache_write(pool, k, v, bt, lens, b.k_scale, b.v_scale)
+            pa.decode(q, pool, bt, lens, b.scale, b.k_scale, b.v_scale, out=out, workspace=ws,
+                      partition_size=64, phase="partials")
+            pa.decode(q, pool, bt, lens, b.scale, b.k_scale, b.v_scale, out=out, workspace=ws,
+                      partition_size=64, phase="merge")
+
+        step()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            out.fill_(float("nan"))
+            pa.decode(q, pool, bt, lens, b.scale, b.k_scale, b.v_scale, partition_size=128)  # eager work
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+        pool1 = oracle.cache_write(pool_np, kvd, b.new_key[0], b.new_value[0], src, bt_np, lens1, 16,
+                                   b.k_scale, b.v_scale)
+        assert np.array_equal(host_bits(pool), pool1)
+        got = oracle.to_f64(host_bits(out), qd)
+        assert_decode_close(got, oracle_decode(b, pool1, b.step_query[0], bt_np, lens1), b)
+
+
 def test_workspace_contents_do_not_matter():
     """The workspace is scratch: garbage on entry, or reuse across calls of
     other sizes, changes nothing."""
