@@ -80,6 +80,10 @@ __device__ __forceinline__ uint4 stream_load(const uint8_t* p) {
     return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
 
+__device__ __forceinline__ uint4 cached_load(const uint8_t* p) {
+    return __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -273,11 +277,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     // the 4 waves; every wave keeps NS chunks of loads in flight, issuing
     // chunk c + (NS-1)*4 right before it consumes chunk c.  Loads past the
     // wave's last chunk re-read a valid chunk and are masked out (nvalid 0).
+    //
+    // Blocks that a neighbouring sequence (s - 1 or s + 1) maps at the same
+    // logical index -- a shared prefix -- will be read again by that
+    // sequence's workgroups at about the same time: they are loaded through
+    // the caches.  Every other block is streamed with nontemporal loads.
     const int lb_first = t_begin >> shift;
     const int lb_last = (t_end - 1) >> shift;
     for (int seg0 = lb_first; seg0 <= lb_last; seg0 += 64) {
         const int seg_blocks = min(64, lb_last - seg0 + 1);
-        const int my_blk = lane < seg_blocks ? bt_row[seg0 + lane] : 0;
+        const bool in_seg = lane < seg_blocks;
+        const int my_blk = in_seg ? bt_row[seg0 + lane] : 0;
+        const int prev_blk = in_seg && s > 0 ? bt_row[seg0 + lane - a.max_blocks_per_seq] : -1;
+        const int next_blk = in_seg && s + 1 < a.num_seqs ? bt_row[seg0 + lane + a.max_blocks_per_seq] : -1;
+        const uint64_t shared = __builtin_amdgcn_ballot_w64(in_seg && (my_blk == prev_blk || my_blk == next_blk));
         const int seg_t0 = max(t_begin, seg0 << shift);
         const int seg_t1 = min(t_end, (seg0 + seg_blocks) << shift);
         const int n_chunks = (seg_t1 - seg_t0 + TPC - 1) / TPC;
@@ -292,16 +305,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
             const int nvalid = (c < n_chunks && blk_ok) ? min(TPC, seg_t1 - tc) : 0;
             const int64_t row0 = ((int64_t)(blk_ok ? blk : 0) * 2 << shift) + (tc & (a.block_size - 1));
             const uint8_t* kbase = pool + row0 * row_bytes;
+            auto load_chunk = [&](auto load) {
 #pragma unroll
-            for (int i = 0; i < TPC; ++i) {
-                const uint32_t ti = (uint32_t)(i < nvalid ? i : 0) * row_bytes;
-                kr[i] = stream_load(kbase + ti + lane_off);
-            }
+                for (int i = 0; i < TPC; ++i) {
+                    const uint32_t ti = (uint32_t)(i < nvalid ? i : 0) * row_bytes;
+                    kr[i] = load(kbase + ti + lane_off);
+                }
 #pragma unroll
-            for (int i = 0; i < TPC; ++i) {
-                const uint32_t ti = (uint32_t)(i < nvalid ? i : 0) * row_bytes;
-                vr[i] = stream_load(kbase + half_bytes + ti + lane_off);
-            }
+                for (int i = 0; i < TPC; ++i) {
+                    const uint32_t ti = (uint32_t)(i < nvalid ? i : 0) * row_bytes;
+                    vr[i] = load(kbase + half_bytes + ti + lane_off);
+                }
+            };
+            if ((shared >> ((tc >> shift) - seg0)) & 1) load_chunk(cached_load);
+            else load_chunk(stream_load);
             return nvalid;
         };
 

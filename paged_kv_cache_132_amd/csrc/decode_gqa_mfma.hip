@@ -62,6 +62,10 @@ __device__ __forceinline__ uint4 stream_load(const uint8_t* p) {
     return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
 
+__device__ __forceinline__ uint4 cached_load(const uint8_t* p) {
+    return __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4*>(p));
+}
+
 // 8 fp8 codes (two dwords) -> 8 bf16, exactly.
 __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
     const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
@@ -149,7 +153,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     const int lb_last = (t_end - 1) >> shift;
     for (int seg0 = lb_first; seg0 <= lb_last; seg0 += 64) {
         const int seg_blocks = min(64, lb_last - seg0 + 1);
-        const int my_blk = lane < seg_blocks ? bt_row[seg0 + lane] : 0;
+        const bool in_seg = lane < seg_blocks;
+        const int my_blk = in_seg ? bt_row[seg0 + lane] : 0;
+        // blocks a neighbouring sequence maps at the same logical index (a
+        // shared prefix) go through the caches; the rest are streamed
+        const int prev_blk = in_seg && s > 0 ? bt_row[seg0 + lane - a.max_blocks_per_seq] : -1;
+        const int next_blk = in_seg && s + 1 < a.num_seqs ? bt_row[seg0 + lane + a.max_blocks_per_seq] : -1;
+        const uint64_t shared = __builtin_amdgcn_ballot_w64(in_seg && (my_blk == prev_blk || my_blk == next_blk));
         const int seg_t0 = max(t_begin, seg0 << shift);
         const int seg_t1 = min(t_end, (seg0 + seg_blocks) << shift);
         const int n_steps = (seg_t1 - seg_t0 + kStepTokens - 1) / kStepTokens;
@@ -167,15 +177,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
                 const int th = min(t0 + 16 * u, seg_t1 - 1) & ~15;       // half start (clamped into range)
                 const int blk = __builtin_amdgcn_readlane(my_blk, (th >> shift) - seg0);
                 const bool ok = blk >= 0 && blk < a.num_blocks;
+                auto load_half = [&](auto load) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int t = th + 8 * j + (lane >> 3);
-                    const int tok = t < seg_t1 ? t : th;
-                    const int64_t row = ((int64_t)(ok ? blk : 0) * 2 << shift) + (tok & (a.block_size - 1));
-                    const uint8_t* kp = pool + row * row_bytes + lane_col;
-                    kr[2 * u + j] = stream_load(kp);
-                    vr[2 * u + j] = stream_load(kp + half_bytes);
-                }
+                    for (int j = 0; j < 2; ++j) {
+                        const int t = th + 8 * j + (lane >> 3);
+                        const int tok = t < seg_t1 ? t : th;
+                        const int64_t row = ((int64_t)(ok ? blk : 0) * 2 << shift) + (tok & (a.block_size - 1));
+                        const uint8_t* kp = pool + row * row_bytes + lane_col;
+                        kr[2 * u + j] = load(kp);
+                        vr[2 * u + j] = load(kp + half_bytes);
+                    }
+                };
+                if ((shared >> ((th >> shift) - seg0)) & 1) load_half(cached_load);
+                else load_half(stream_load);
             }
         };
 
