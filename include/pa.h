@@ -196,6 +196,36 @@ pa_status pa_decode_merge(void* out, const void* query, pa_dtype q_dtype,
                           int32_t partition_size, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * pa_copy_blocks -- copy whole KV blocks from one pool to another of the same
+ * block geometry: for each pair i, block block_mapping[2i + 1] of dst_pool
+ * becomes a byte copy of block block_mapping[2i] of src_pool (K half and V
+ * half, every head: 2 * block_size * num_kv_heads * head_dim elements of
+ * kv_dtype).  It serves the copy-on-write of a shared block before a branch
+ * writes into it ([nano-vllm blog §4.3]; src_pool == dst_pool) and the swap
+ * of a preempted request's blocks out to CPU memory and back in
+ * ([nano-vllm blog §2.2]; one pool in pinned host memory).
+ *
+ *   src_pool, dst_pool  [src_num_blocks | dst_num_blocks, 2, block_size,
+ *                       num_kv_heads, head_dim]; each is device memory of the
+ *                       current device or host memory allocated pinned
+ *                       (hipHostMalloc); anything else -> PA_ERR_UNSUPPORTED.
+ *   block_mapping       device int32 [num_pairs, 2]: (source, destination).
+ *                       No destination may appear twice, and within one pool
+ *                       no block may be both a source and a destination
+ *                       (pairs run in parallel).  Pairs with an id outside
+ *                       its pool are skipped.
+ *
+ * Asynchronous on `stream`; num_pairs == 0 enqueues nothing.  Errors:
+ * NULL_POINTER, MISALIGNED (pools and mapping need 16-byte alignment),
+ * BAD_SHAPE (non-positive sizes, negative num_pairs), BAD_DTYPE,
+ * UNSUPPORTED, HIP (launch failure).
+ */
+pa_status pa_copy_blocks(const void* src_pool, int32_t src_num_blocks, void* dst_pool,
+                         int32_t dst_num_blocks, pa_dtype kv_dtype, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, const int32_t* block_mapping,
+                         int32_t num_pairs, void* stream);
+
 /* Human-readable name of a status value (static storage, never NULL). */
 const char* pa_status_string(pa_status status);
 

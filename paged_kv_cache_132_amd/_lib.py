@@ -20,7 +20,7 @@ STATUS_NAMES = {
     0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
     4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_MISALIGNED", 6: "PA_ERR_WORKSPACE_TOO_SMALL", 7: "PA_ERR_HIP",
 }
-EXPORTED = ("pa_cache_write", "pa_decode", "pa_decode_partials", "pa_decode_merge",
+EXPORTED = ("pa_cache_write", "pa_copy_blocks", "pa_decode", "pa_decode_partials", "pa_decode_merge",
             "pa_decode_workspace_size", "pa_decode_partition_size", "pa_status_string")
 
 _lib = None
@@ -44,6 +44,8 @@ def load() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
             fn.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                            i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, vp, sz, vp]
+        lib.pa_copy_blocks.restype = ctypes.c_int
+        lib.pa_copy_blocks.argtypes = [vp, i32, vp, i32, ctypes.c_int, i32, i32, i32, vp, i32, vp]
         lib.pa_decode_workspace_size.restype = sz
         lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
         lib.pa_decode_partition_size.restype = i32
@@ -113,6 +115,23 @@ def cache_write(kv_pool: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                                _ptr(block_tables), _ptr(context_lens), B, hkv, d, bs, mb, nb,
                                float(k_scale), float(v_scale), _stream(stream))
     _check(st, "pa_cache_write")
+
+
+def copy_blocks(src_pool: torch.Tensor, dst_pool: torch.Tensor, block_mapping: torch.Tensor,
+                stream=None) -> None:
+    """dst_pool[d] = src_pool[s] for each row (s, d) of block_mapping (int32
+    [num_pairs, 2] on the device).  Either pool may be pinned host memory
+    (a swap); pass one tensor as both for copy-on-write inside a pool."""
+    nb_s, bs, hkv, d = _pool_dims(src_pool)
+    nb_d, bs_d, hkv_d, d_d = _pool_dims(dst_pool)
+    if (bs, hkv, d) != (bs_d, hkv_d, d_d) or src_pool.dtype != dst_pool.dtype:
+        raise ValueError("pools must have the same block geometry and dtype")
+    if block_mapping.dtype != torch.int32 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2 \
+            or not block_mapping.is_contiguous():
+        raise ValueError("block_mapping must be a contiguous int32 [num_pairs, 2] tensor")
+    st = load().pa_copy_blocks(_ptr(src_pool), nb_s, _ptr(dst_pool), nb_d, pa_dtype(src_pool), bs, hkv, d,
+                               _ptr(block_mapping), int(block_mapping.shape[0]), _stream(stream))
+    _check(st, "pa_copy_blocks")
 
 
 def decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,

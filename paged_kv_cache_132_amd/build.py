@@ -19,7 +19,7 @@ INCLUDE = os.path.join(REPO, "include")
 LIB = os.path.join(PKG, "libpa.so")
 BENCH_LIB = os.path.join(PKG, "libpa_bench.so")
 
-SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "decode_gqa_mfma.hip"]
+SOURCES = ["pa_api.cpp", "cache_write.hip", "copy_blocks.hip", "decode.hip", "decode_gqa_mfma.hip"]
 BENCH_SOURCES = ["bench_util.hip"]
 
 

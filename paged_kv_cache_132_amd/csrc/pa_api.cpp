@@ -16,6 +16,7 @@ namespace {
 bool known_dtype(pa_dtype d) { return d == PA_F16 || d == PA_BF16 || d == PA_FP8_E4M3; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int elem_bytes(pa_dtype d) { return d == PA_FP8_E4M3 ? 1 : 2; }
 
 int log2_exact(int x) {
     int s = 0;
@@ -192,6 +193,57 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
                      kv_dtype, partition_size, &p))
         return 0;
     return p.bytes;
+}
+
+// Device address of a pool: device memory of the current device, or host
+// memory allocated pinned (hipHostMalloc), which kernels reach through the
+// same virtual address.  Anything else (pageable host memory, another
+// device's memory) is refused rather than handed to a kernel.
+static bool pool_device_address(const void* p, const void** out) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();                       // do not leave the error for a later check
+        return false;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (attr.type == hipMemoryTypeDevice && attr.device == dev) {
+        *out = p;
+        return true;
+    }
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer == p) {
+        *out = p;
+        return true;
+    }
+    return false;
+}
+
+pa_status pa_copy_blocks(const void* src_pool, int32_t src_num_blocks, void* dst_pool,
+                         int32_t dst_num_blocks, pa_dtype kv_dtype, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, const int32_t* block_mapping,
+                         int32_t num_pairs, void* stream) {
+    if (!known_dtype(kv_dtype)) return PA_ERR_BAD_DTYPE;
+    if (src_num_blocks <= 0 || dst_num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || num_pairs < 0)
+        return PA_ERR_BAD_SHAPE;
+    const int64_t block_bytes = (int64_t)2 * block_size * num_kv_heads * head_dim * elem_bytes(kv_dtype);
+    if (block_bytes % 16 != 0) return PA_ERR_BAD_SHAPE;
+    if (num_pairs == 0) return PA_OK;
+    if (!src_pool || !dst_pool || !block_mapping) return PA_ERR_NULL_POINTER;
+    if (!aligned16(src_pool) || !aligned16(dst_pool) || !aligned16(block_mapping)) return PA_ERR_MISALIGNED;
+    const void* src_dev = nullptr;
+    const void* dst_dev = nullptr;
+    if (!pool_device_address(src_pool, &src_dev) || !pool_device_address(dst_pool, &dst_dev))
+        return PA_ERR_UNSUPPORTED;
+    CopyArgs a;
+    a.src = static_cast<const uint8_t*>(src_dev);
+    a.dst = static_cast<uint8_t*>(const_cast<void*>(dst_dev));
+    a.mapping = block_mapping;
+    a.num_pairs = num_pairs;
+    a.block_bytes = block_bytes;
+    a.src_num_blocks = src_num_blocks;
+    a.dst_num_blocks = dst_num_blocks;
+    return launch_copy_blocks(a, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
 static pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,

@@ -80,6 +80,14 @@ struct WriteArgs {
     float k_scale, v_scale;
 };
 
+struct CopyArgs {
+    const uint8_t* src;      // device address of the source pool
+    uint8_t* dst;            // device address of the destination pool
+    const int32_t* mapping;  // [num_pairs, 2]: (source block, destination block)
+    int64_t num_pairs, block_bytes;
+    int32_t src_num_blocks, dst_num_blocks;
+};
+
 // Launchers (defined next to their kernels).  Return the hipError_t as int.
 // phase bit 1: attention pass (partials), bit 2: split-K merge.
 constexpr int kPhasePartials = 1;
@@ -88,5 +96,6 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
                   int head_dim, int group_size, int phases, void* stream);
 int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream);
 int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream);
+int launch_copy_blocks(const CopyArgs& a, void* stream);
 
 }  // namespace pa

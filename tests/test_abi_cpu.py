@@ -157,3 +157,32 @@ def test_workspace_and_partition_plan(lib):
     assert lib.pa_decode_workspace_size(0, 32, 32, 128, 16, 128, F16, 0) > 0
     with pytest.raises(RuntimeError):
         pa.decode_workspace_size(32, 32, 32, 100, 16, 128, F16)
+
+
+def call_copy(lib, **kw):
+    a = dict(src=FAKE, src_nb=8, dst=FAKE, dst_nb=8, kv_dtype=F16, block_size=16, num_kv_heads=4,
+             head_dim=64, mapping=FAKE, num_pairs=3, stream=None)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["src"], a["src_nb"], a["dst"], a["dst_nb"], a["kv_dtype"], a["block_size"],
+                              a["num_kv_heads"], a["head_dim"], a["mapping"], a["num_pairs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), NULLP),
+    (dict(dst=None), NULLP),
+    (dict(mapping=None), NULLP),
+    (dict(src=FAKE + 8), MISAL),
+    (dict(mapping=FAKE + 4), MISAL),
+    (dict(kv_dtype=5), DTYPE),
+    (dict(src_nb=0), SHAPE),
+    (dict(dst_nb=-1), SHAPE),
+    (dict(num_pairs=-1), SHAPE),
+    (dict(block_size=0), SHAPE),
+    (dict(kv_dtype=FP8, block_size=1, num_kv_heads=1, head_dim=4), SHAPE),   # 8-byte blocks
+])
+def test_copy_blocks_rejects_bad_arguments(lib, kw, status):
+    assert call_copy(lib, **kw) == status
+
+
+def test_copy_blocks_zero_pairs_is_a_noop(lib):
+    assert call_copy(lib, num_pairs=0, src=None, dst=None, mapping=None) == 0
