@@ -197,6 +197,56 @@ pa_status pa_decode_merge(void* out, const void* query, pa_dtype q_dtype,
                           void* stream);
 
 /*
+ * pa_cache_write_tokens -- the prompt-stage write: put a packed run of new
+ * tokens per sequence into the pool ([CANN notes §3.1] packed layout,
+ * [CANN notes §4.2] prompt write into block offsets; [nano-vllm blog §4.3]
+ * only the uncached tail of a prompt is written).
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_dim] of src_dtype; the new
+ *                 tokens of sequence s are rows cu_seqlens[s] ..
+ *                 cu_seqlens[s+1]-1, in order.
+ *   cu_seqlens    device int32 [num_seqs + 1], non-decreasing, from 0;
+ *                 n_s = cu_seqlens[s+1] - cu_seqlens[s].
+ *   context_lens  lengths AFTER the append: row i of sequence s is written at
+ *                 position L_s - n_s + i (block block_tables[s][t / bs],
+ *                 offset t % bs).  Rows with a negative position, rows past
+ *                 cu_seqlens[num_seqs] and table entries outside the pool
+ *                 are skipped.
+ * Everything else (dtypes, fp8 encoding, shapes, alignment, errors) is as in
+ * pa_cache_write, which is this call with one new token per sequence.
+ */
+pa_status pa_cache_write_tokens(void* kv_pool, pa_dtype kv_dtype, const void* key, const void* value,
+                                pa_dtype src_dtype, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* cu_seqlens, int32_t num_seqs,
+                                int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_prefill -- causal attention of packed new queries over the paged pool
+ * ([CANN notes §3.1-3.3]: cu_seqlens bounds each sequence, queries see only
+ * their own sequence and only keys not after their own position, K/V are
+ * found through the block table; [nano-vllm blog §4.3]: the tail of a
+ * prompt whose prefix is cached attends to that prefix too).
+ *
+ *   out, query    [num_tokens, num_heads, head_dim] of q_dtype (out may not
+ *                 alias query); rows as in pa_cache_write_tokens.
+ *   context_lens  lengths with the new tokens included; the n_s new queries
+ *                 of sequence s sit at positions L_s - n_s .. L_s - 1 and
+ *                 query i attends to keys 0 .. L_s - n_s + i.
+ *   max_new_tokens  an upper bound on every n_s (sizes the launch grid).
+ *   The pool must already hold the new tokens (pa_cache_write_tokens first,
+ *   on the same stream).
+ * No workspace.  Supported combinations, scales and errors as in pa_decode.
+ * Sequences with n_s = 0, or with n_s > L_s, produce no output rows.
+ */
+pa_status pa_prefill(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool, pa_dtype kv_dtype,
+                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens,
+                     int32_t num_seqs, int32_t num_tokens, int32_t max_new_tokens, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int32_t num_blocks, float scale, float k_scale, float v_scale, void* stream);
+
+/*
  * pa_copy_blocks -- copy whole KV blocks from one pool to another of the same
  * block geometry: for each pair i, block block_mapping[2i + 1] of dst_pool
  * becomes a byte copy of block block_mapping[2i] of src_pool (K half and V

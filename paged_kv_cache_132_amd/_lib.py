@@ -20,8 +20,9 @@ STATUS_NAMES = {
     0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
     4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_MISALIGNED", 6: "PA_ERR_WORKSPACE_TOO_SMALL", 7: "PA_ERR_HIP",
 }
-EXPORTED = ("pa_cache_write", "pa_copy_blocks", "pa_decode", "pa_decode_partials", "pa_decode_merge",
-            "pa_decode_workspace_size", "pa_decode_partition_size", "pa_status_string")
+EXPORTED = ("pa_cache_write", "pa_cache_write_tokens", "pa_copy_blocks", "pa_decode", "pa_decode_partials",
+            "pa_decode_merge", "pa_decode_workspace_size", "pa_decode_partition_size", "pa_prefill",
+            "pa_status_string")
 
 _lib = None
 _lock = threading.Lock()
@@ -44,6 +45,12 @@ def load() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
             fn.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                            i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, vp, sz, vp]
+        lib.pa_cache_write_tokens.restype = ctypes.c_int
+        lib.pa_cache_write_tokens.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp,
+                                              i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+        lib.pa_prefill.restype = ctypes.c_int
+        lib.pa_prefill.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp,
+                                   i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, vp]
         lib.pa_copy_blocks.restype = ctypes.c_int
         lib.pa_copy_blocks.argtypes = [vp, i32, vp, i32, ctypes.c_int, i32, i32, i32, vp, i32, vp]
         lib.pa_decode_workspace_size.restype = sz
@@ -115,6 +122,66 @@ def cache_write(kv_pool: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                                _ptr(block_tables), _ptr(context_lens), B, hkv, d, bs, mb, nb,
                                float(k_scale), float(v_scale), _stream(stream))
     _check(st, "pa_cache_write")
+
+
+def _cu(cu_seqlens: torch.Tensor, num_seqs: int) -> None:
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.shape != (num_seqs + 1,) or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 [num_seqs + 1] tensor")
+
+
+def _max_new(cu_seqlens: torch.Tensor, max_new_tokens) -> int:
+    """An upper bound on the per-sequence new-token counts; read from the
+    device (a synchronisation) when the caller does not give one."""
+    if max_new_tokens is not None:
+        return int(max_new_tokens)
+    if cu_seqlens.numel() < 2:
+        return 0
+    return int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+
+
+def cache_write_tokens(kv_pool: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor, cu_seqlens: torch.Tensor,
+                       k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """Write packed new tokens (rows cu_seqlens[s] .. cu_seqlens[s+1]-1 of key/value
+    belong to sequence s, at positions context_lens[s] - n_s ..) into kv_pool in place."""
+    nb, bs, hkv, d = _pool_dims(kv_pool)
+    if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (hkv, d):
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim] matching the pool")
+    if not (key.is_contiguous() and value.is_contiguous()) or key.dtype != value.dtype:
+        raise ValueError("key/value must be contiguous and of one dtype")
+    B = int(context_lens.shape[0])
+    mb = _tables(block_tables, context_lens, B)
+    _cu(cu_seqlens, B)
+    st = load().pa_cache_write_tokens(_ptr(kv_pool), pa_dtype(kv_pool), _ptr(key), _ptr(value), pa_dtype(key),
+                                      _ptr(block_tables), _ptr(context_lens), _ptr(cu_seqlens), B,
+                                      int(key.shape[0]), hkv, d, bs, mb, nb, float(k_scale), float(v_scale),
+                                      _stream(stream))
+    _check(st, "pa_cache_write_tokens")
+
+
+def prefill(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tensor,
+            context_lens: torch.Tensor, cu_seqlens: torch.Tensor, scale: float, k_scale: float = 1.0,
+            v_scale: float = 1.0, max_new_tokens: int | None = None, out: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """Causal attention of packed new queries [num_tokens, num_heads, head_dim] over
+    their own sequences in the paged pool; returns out of query's shape and dtype."""
+    nb, bs, hkv, d = _pool_dims(kv_pool)
+    if query.dim() != 3 or query.shape[2] != d or not query.is_contiguous():
+        raise ValueError("query must be a contiguous [num_tokens, num_heads, head_dim] tensor")
+    T, hq = int(query.shape[0]), int(query.shape[1])
+    B = int(context_lens.shape[0])
+    mb = _tables(block_tables, context_lens, B)
+    _cu(cu_seqlens, B)
+    if out is None:
+        out = torch.empty_like(query)
+    elif out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
+        raise ValueError("out must match query")
+    st = load().pa_prefill(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), pa_dtype(kv_pool),
+                           _ptr(block_tables), _ptr(context_lens), _ptr(cu_seqlens), B, T,
+                           _max_new(cu_seqlens, max_new_tokens), hq, hkv, d, bs, mb, nb, float(scale),
+                           float(k_scale), float(v_scale), _stream(stream))
+    _check(st, "pa_prefill")
+    return out
 
 
 def copy_blocks(src_pool: torch.Tensor, dst_pool: torch.Tensor, block_mapping: torch.Tensor,

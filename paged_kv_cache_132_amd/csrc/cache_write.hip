@@ -1,10 +1,14 @@
-// pa_cache_write kernels: put each sequence's newest K/V row into its paged
-// slot ([nano-vllm blog §4.1 step 3], [CANN notes §4.3 steps 1-3]).
+// pa_cache_write / pa_cache_write_tokens kernels: put new K/V rows into their
+// paged slots -- each sequence's newest token in the decode step
+// ([nano-vllm blog §4.1 step 3], [CANN notes §4.3 steps 1-3]), or a packed
+// run of new tokens per sequence in the prompt stage ([CANN notes §3.1,
+// §4.2]: token i of sequence s's run sits at position L_s - n_s + i, so the
+// last block is written only as far as the tokens it holds).
 //
 // One thread moves 8 elements (16 bytes of a 16-bit source row).  Consecutive
-// threads cover consecutive 16-byte pieces of one (sequence, KV head, K|V)
-// row, so each row is one contiguous, fully coalesced segment on both sides.
-// The work is a few hundred KiB per step; the kernel is latency-bound.
+// threads cover consecutive 16-byte pieces of one (row, KV head, K|V) row, so
+// each row is one contiguous, fully coalesced segment on both sides.  A
+// packed row finds its sequence by binary search over cu_seqlens.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -52,7 +56,7 @@ __device__ __forceinline__ uint32_t e4m3_from_float(float y) {
 template <int SRC, int KVT>
 __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a) {
     const int chunks = a.head_dim / kElemsPerThread;
-    const int64_t total = (int64_t)a.num_seqs * a.num_kv_heads * 2 * chunks;
+    const int64_t total = (int64_t)a.num_rows * a.num_kv_heads * 2 * chunks;
     const int64_t i = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
     if (i >= total) return;
     const int c = (int)(i % chunks);
@@ -60,18 +64,34 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
     const int kv = (int)(rest & 1);
     rest >>= 1;
     const int g = (int)(rest % a.num_kv_heads);
-    const int s = (int)(rest / a.num_kv_heads);
+    const int row = (int)(rest / a.num_kv_heads);
 
-    const int L = a.context_lens[s];
-    if (L <= 0) return;
-    const int t = L - 1;
+    int s, t;
+    if (a.cu_seqlens == nullptr) {
+        s = row;
+        t = a.context_lens[s] - 1;
+    } else {
+        // the sequence whose run holds this row: largest s with cu[s] <= row
+        if (row >= a.cu_seqlens[a.num_seqs]) return;
+        int lo = 0, hi = a.num_seqs;                 // cu[lo] <= row < cu[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.cu_seqlens[mid] <= row) lo = mid;
+            else hi = mid;
+        }
+        s = lo;
+        const int first = a.cu_seqlens[s];
+        const int n = a.cu_seqlens[s + 1] - first;
+        t = a.context_lens[s] - n + (row - first);
+    }
+    if (t < 0) return;
     const int lb = t / a.block_size;
     if (lb >= a.max_blocks_per_seq) return;
     const int blk = a.block_tables[(int64_t)s * a.max_blocks_per_seq + lb];
     if (blk < 0 || blk >= a.num_blocks) return;
     const int off = t - lb * a.block_size;
 
-    const int64_t src_elem = ((int64_t)s * a.num_kv_heads + g) * a.head_dim + c * kElemsPerThread;
+    const int64_t src_elem = ((int64_t)row * a.num_kv_heads + g) * a.head_dim + c * kElemsPerThread;
     const int64_t dst_elem =
         (((int64_t)blk * 2 + kv) * a.block_size + off) * (int64_t)a.num_kv_heads * a.head_dim +
         (int64_t)g * a.head_dim + c * kElemsPerThread;
@@ -97,8 +117,9 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
 
 template <int SRC, int KVT>
 int launch_typed(const WriteArgs& a, hipStream_t stream) {
-    const int64_t total = (int64_t)a.num_seqs * a.num_kv_heads * 2 * (a.head_dim / kElemsPerThread);
+    const int64_t total = (int64_t)a.num_rows * a.num_kv_heads * 2 * (a.head_dim / kElemsPerThread);
     const int64_t blocks = (total + kWriteThreads - 1) / kWriteThreads;
+    if (blocks == 0) return 0;
     hipLaunchKernelGGL((cache_write_kernel<SRC, KVT>), dim3((unsigned)blocks), dim3(kWriteThreads),
                        0, stream, a);
     return (int)hipGetLastError();

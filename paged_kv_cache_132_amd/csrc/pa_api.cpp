@@ -134,11 +134,12 @@ const char* pa_status_string(pa_status status) {
     return "PA_ERR_UNKNOWN";
 }
 
-pa_status pa_cache_write(void* kv_pool, pa_dtype kv_dtype, const void* key, const void* value,
-                         pa_dtype src_dtype, const int32_t* block_tables,
-                         const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
-                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                         int32_t num_blocks, float k_scale, float v_scale, void* stream) {
+static pa_status cache_write_rows(void* kv_pool, pa_dtype kv_dtype, const void* key, const void* value,
+                                  pa_dtype src_dtype, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* cu_seqlens, int32_t num_seqs,
+                                  int32_t num_rows, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                  float k_scale, float v_scale, void* stream) {
     if (!known_dtype(kv_dtype) || !known_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
     if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         max_blocks_per_seq <= 0 || num_blocks <= 0)
@@ -151,8 +152,9 @@ pa_status pa_cache_write(void* kv_pool, pa_dtype kv_dtype, const void* key, cons
     if (kv_dtype == PA_FP8_E4M3 &&
         !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
         return PA_ERR_BAD_SHAPE;
-    if ((int64_t)num_seqs * num_kv_heads * head_dim * 2 > (int64_t)INT32_MAX) return PA_ERR_BAD_SHAPE;
-    if (num_seqs == 0) return PA_OK;
+    if (num_rows < 0) return PA_ERR_BAD_SHAPE;
+    if ((int64_t)num_rows * num_kv_heads * head_dim * 2 > (int64_t)INT32_MAX) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || num_rows == 0) return PA_OK;
     if (!kv_pool || !key || !value || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
     if (!aligned16(kv_pool) || !aligned16(key) || !aligned16(value) || !aligned16(block_tables) ||
         !aligned16(context_lens))
@@ -164,7 +166,9 @@ pa_status pa_cache_write(void* kv_pool, pa_dtype kv_dtype, const void* key, cons
     a.value = value;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
+    a.cu_seqlens = cu_seqlens;
     a.num_seqs = num_seqs;
+    a.num_rows = num_rows;
     a.num_kv_heads = num_kv_heads;
     a.head_dim = head_dim;
     a.block_size = block_size;
@@ -173,6 +177,31 @@ pa_status pa_cache_write(void* kv_pool, pa_dtype kv_dtype, const void* key, cons
     a.k_scale = k_scale;
     a.v_scale = v_scale;
     return launch_cache_write(a, src_dtype, kv_dtype, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_cache_write(void* kv_pool, pa_dtype kv_dtype, const void* key, const void* value,
+                         pa_dtype src_dtype, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int32_t num_blocks, float k_scale, float v_scale, void* stream) {
+    return cache_write_rows(kv_pool, kv_dtype, key, value, src_dtype, block_tables, context_lens, nullptr,
+                            num_seqs, num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            num_blocks, k_scale, v_scale, stream);
+}
+
+pa_status pa_cache_write_tokens(void* kv_pool, pa_dtype kv_dtype, const void* key, const void* value,
+                                pa_dtype src_dtype, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* cu_seqlens, int32_t num_seqs,
+                                int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                float k_scale, float v_scale, void* stream) {
+    if (num_seqs > 0 && num_tokens > 0) {
+        if (!cu_seqlens) return PA_ERR_NULL_POINTER;
+        if (!aligned16(cu_seqlens)) return PA_ERR_MISALIGNED;
+    }
+    return cache_write_rows(kv_pool, kv_dtype, key, value, src_dtype, block_tables, context_lens, cu_seqlens,
+                            num_seqs, num_tokens, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            num_blocks, k_scale, v_scale, stream);
 }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -193,6 +222,44 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
                      kv_dtype, partition_size, &p))
         return 0;
     return p.bytes;
+}
+
+pa_status pa_prefill(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool, pa_dtype kv_dtype,
+                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens,
+                     int32_t num_seqs, int32_t num_tokens, int32_t max_new_tokens, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int32_t num_blocks, float scale, float k_scale, float v_scale, void* stream) {
+    // the per-call checks are those of pa_decode, with no split-K partition
+    pa_status st = check_decode_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens,
+                                     num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                     max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, 0);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0 || max_new_tokens < 0) return PA_ERR_BAD_SHAPE;
+    if ((int64_t)num_tokens * num_heads * head_dim > (int64_t)INT32_MAX * 8) return PA_ERR_BAD_SHAPE;
+    const int group = num_heads / num_kv_heads;
+    if (prefill_grid(num_seqs, num_kv_heads, group, max_new_tokens) > (int64_t)INT32_MAX) return PA_ERR_BAD_SHAPE;
+    if (num_seqs == 0 || num_tokens == 0 || max_new_tokens == 0) return PA_OK;
+    if (!cu_seqlens) return PA_ERR_NULL_POINTER;
+    if (!aligned16(cu_seqlens)) return PA_ERR_MISALIGNED;
+    const bool fp8 = kv_dtype == PA_FP8_E4M3;
+    PrefillArgs a;
+    a.out = out;
+    a.query = query;
+    a.kv_pool = kv_pool;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.cu_seqlens = cu_seqlens;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.block_shift = log2_exact(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
+    a.v_scale = fp8 ? v_scale : 1.0f;
+    return launch_prefill(a, kv_dtype, head_dim, group, max_new_tokens, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
 // Device address of a pool: device memory of the current device, or host

@@ -72,12 +72,27 @@ struct DecodeArgs {
 
 struct WriteArgs {
     void* kv_pool;
-    const void* key;
+    const void* key;            // [num_rows, num_kv_heads, head_dim]
     const void* value;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    int32_t num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks;
+    const int32_t* cu_seqlens;  // packed runs of new tokens; null: one token per sequence
+    int32_t num_seqs, num_rows;
+    int32_t num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks;
     float k_scale, v_scale;
+};
+
+struct PrefillArgs {
+    void* out;                  // [num_tokens, num_heads, head_dim], query dtype
+    const void* query;          // [num_tokens, num_heads, head_dim]
+    const void* kv_pool;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const int32_t* cu_seqlens;  // [num_seqs + 1]
+    int32_t num_seqs, num_tokens, num_heads, num_kv_heads;
+    int32_t block_size, block_shift, max_blocks_per_seq, num_blocks;
+    float score_scale;          // scale * k_scale * log2(e)
+    float v_scale;
 };
 
 struct CopyArgs {
@@ -97,5 +112,8 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
 int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream);
 int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream);
 int launch_copy_blocks(const CopyArgs& a, void* stream);
+int64_t prefill_grid(int num_seqs, int num_kv_heads, int group_size, int max_new_tokens);
+int launch_prefill(const PrefillArgs& a, pa_dtype kv_dtype, int head_dim, int group_size, int max_new_tokens,
+                   void* stream);
 
 }  // namespace pa

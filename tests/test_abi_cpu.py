@@ -186,3 +186,65 @@ def test_copy_blocks_rejects_bad_arguments(lib, kw, status):
 
 def test_copy_blocks_zero_pairs_is_a_noop(lib):
     assert call_copy(lib, num_pairs=0, src=None, dst=None, mapping=None) == 0
+
+
+def call_write_tokens(lib, **kw):
+    a = dict(kv_pool=FAKE, kv_dtype=F16, key=FAKE, value=FAKE, src_dtype=F16, block_tables=FAKE,
+             context_lens=FAKE, cu_seqlens=FAKE, num_seqs=4, num_tokens=20, num_kv_heads=8, head_dim=64,
+             block_size=16, max_blocks_per_seq=3, num_blocks=64, k_scale=1.0, v_scale=1.0, stream=None)
+    a.update(kw)
+    return lib.pa_cache_write_tokens(a["kv_pool"], a["kv_dtype"], a["key"], a["value"], a["src_dtype"],
+                                     a["block_tables"], a["context_lens"], a["cu_seqlens"], a["num_seqs"],
+                                     a["num_tokens"], a["num_kv_heads"], a["head_dim"], a["block_size"],
+                                     a["max_blocks_per_seq"], a["num_blocks"], a["k_scale"], a["v_scale"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_seqlens=None), NULLP),
+    (dict(key=None), NULLP),
+    (dict(cu_seqlens=FAKE + 4), MISAL),
+    (dict(num_tokens=-1), SHAPE),
+    (dict(src_dtype=FP8), UNSUP),
+    (dict(block_size=8), UNSUP),
+])
+def test_write_tokens_rejects_bad_arguments(lib, kw, status):
+    assert call_write_tokens(lib, **kw) == status
+
+
+def test_write_tokens_without_tokens_is_a_noop(lib):
+    assert call_write_tokens(lib, num_tokens=0, cu_seqlens=None, key=None, value=None) == 0
+    assert call_write_tokens(lib, num_seqs=0, cu_seqlens=None) == 0
+
+
+def call_prefill(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, q_dtype=F16, kv_pool=FAKE, kv_dtype=F16, block_tables=FAKE,
+             context_lens=FAKE, cu_seqlens=FAKE, num_seqs=4, num_tokens=40, max_new_tokens=20,
+             num_heads=8, num_kv_heads=8, head_dim=64, block_size=16, max_blocks_per_seq=3, num_blocks=64,
+             scale=0.125, k_scale=1.0, v_scale=1.0, stream=None)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["query"], a["q_dtype"], a["kv_pool"], a["kv_dtype"], a["block_tables"],
+                          a["context_lens"], a["cu_seqlens"], a["num_seqs"], a["num_tokens"],
+                          a["max_new_tokens"], a["num_heads"], a["num_kv_heads"], a["head_dim"],
+                          a["block_size"], a["max_blocks_per_seq"], a["num_blocks"], a["scale"],
+                          a["k_scale"], a["v_scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_seqlens=None), NULLP),
+    (dict(out=None), NULLP),
+    (dict(cu_seqlens=FAKE + 8), MISAL),
+    (dict(num_tokens=-1), SHAPE),
+    (dict(max_new_tokens=-2), SHAPE),
+    (dict(q_dtype=F16, kv_dtype=FP8), UNSUP),
+    (dict(head_dim=96), UNSUP),
+    (dict(num_heads=24, num_kv_heads=8), UNSUP),
+    (dict(kv_dtype=FP8, q_dtype=BF16, k_scale=0.0), SHAPE),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, status):
+    assert call_prefill(lib, **kw) == status
+
+
+def test_prefill_without_tokens_is_a_noop(lib):
+    assert call_prefill(lib, num_tokens=0, cu_seqlens=None) == 0
+    assert call_prefill(lib, max_new_tokens=0, cu_seqlens=None) == 0

@@ -25,6 +25,7 @@ from .configs import (
     make_custom,
     CONFIG_MAKERS,
 )
+from .prefill import PrefillBatch, make_prefill, make_prefill_mixed
 
 __all__ = [
     "BlockManager",
@@ -38,4 +39,7 @@ __all__ = [
     "make_gqa_fp8",
     "make_custom",
     "CONFIG_MAKERS",
+    "PrefillBatch",
+    "make_prefill",
+    "make_prefill_mixed",
 ]
