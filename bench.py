@@ -294,14 +294,118 @@ def bench_copy_blocks(args, torch, pa) -> int:
     return 0
 
 
+def prefill_flops(b) -> int:
+    """Causal attention multiply-adds x 2: each new query at position p scores
+    and weights p + 1 keys (QK and PV: 2 x 2 x head_dim flops per key) for
+    every query head."""
+    lens = b.context_lens.astype(np.int64)
+    new = b.new_lens.astype(np.int64)
+    keys = sum(int(((L - n + 1) + L) * n // 2) for L, n in zip(lens, new))   # sum of (p + 1)
+    return 4 * b.head_dim * b.num_heads * keys
+
+
+def bench_prefill(args, torch, pa) -> int:
+    """The prompt stage on the packed prompt batch of [CANN notes §1.2]:
+    8 fresh prompts of 128..2048 tokens (5256 in all), 32/32 heads,
+    head_dim 128, fp16, block size 16.  One step = pa_cache_write_tokens of
+    all 5256 tokens + pa_prefill."""
+    import oracle
+    from workloads import make_prefill_mixed
+
+    b = make_prefill_mixed()
+    flops = prefill_flops(b)
+    dev = torch.device("cuda:0")
+    d16 = lambda raw: torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.float16).to(dev)
+    pool = d16(b.kv_pool)
+    bt = torch.from_numpy(b.block_table_array()).to(dev)
+    lens = torch.from_numpy(b.context_lens).to(dev)
+    cu = torch.from_numpy(b.cu_seqlens).to(dev)
+    q, k, v = d16(b.query), d16(b.new_key), d16(b.new_value)
+    out = torch.empty_like(q)
+    mx = int(b.new_lens.max())
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.cache_write_tokens(pool, k, v, bt, lens, cu)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.prefill(q, pool, bt, lens, cu, b.scale, out=out, max_new_tokens=mx)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    write_us = float(np.mean([e[0].elapsed_time(e[1]) for e in events]) * 1e3)
+    attn = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e3
+    attn_us = float(attn.mean())
+    achieved = flops / (attn_us * 1e-6) / 1e12
+    log(f"prefill: attention {attn_us:.1f} us ({achieved:.0f} TFLOP/s), write {write_us:.1f} us, "
+        f"step {ms_step * 1e3:.1f} us")
+    res = {
+        "metric": "paged prefill attention TFLOP/s (causal, packed prompts), 1 GPU",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": b.name, "num_seqs": b.num_seqs, "num_tokens": b.num_tokens,
+                   "num_heads": b.num_heads, "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+                   "block_size": b.block_size, "seed": b.seed},
+        "prefill_kernel_us": round(attn_us, 2),
+        "prefill_kernel_us_p10_p50_p90": [round(float(np.percentile(attn, x)), 2) for x in (10, 50, 90)],
+        "write_tokens_kernel_us": round(write_us, 2),
+        "prefill_tokens_per_s_per_layer": round(b.num_tokens / (ms_step * 1e-3), 1),
+        "flops": flops,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(achieved / 2500.0, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        try:
+            from threadpoolctl import threadpool_limits
+            ctx = threadpool_limits(limits=1)
+        except ImportError:                  # pragma: no cover
+            ctx = None
+        done, f_done, t_total = 0, 0, 0.0
+        try:
+            for s in np.argsort(b.new_lens):  # shortest prompts first, until the budget is spent
+                lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
+                t1 = time.perf_counter()
+                oracle.paged_prefill(b.query[lo:hi], "f16", b.kv_pool, "f16", b.block_table_array()[s:s + 1],
+                                     b.context_lens[s:s + 1], np.array([0, hi - lo]), b.block_size, b.scale)
+                t_total += time.perf_counter() - t1
+                done += 1
+                n = hi - lo
+                f_done += 4 * b.head_dim * b.num_heads * n * (n + 1) // 2
+                if t_total >= min(args.cpu_budget, 15.0):
+                    break
+        finally:
+            if ctx is not None:
+                ctx.__exit__(None, None, None)
+        res["cpu_baseline"] = {"value": round(f_done / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{done} of {b.num_seqs} prompts (shortest first), float64 numpy, "
+                                         f"{t_total:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama7b")
-    ap.add_argument("--op", default="decode", choices=("decode", "copy_blocks"),
-                    help="decode: the decode step (default); copy_blocks: the block-copy kernel")
+    ap.add_argument("--op", default="decode", choices=("decode", "copy_blocks", "prefill"),
+                    help="decode: the decode step (default); copy_blocks: the block-copy kernel; "
+                         "prefill: the prompt stage (multi-token write + causal prefill)")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -326,6 +430,8 @@ def main() -> int:
         return copy_calibration(torch, args.steps)
     if args.op == "copy_blocks":
         return bench_copy_blocks(args, torch, pa)
+    if args.op == "prefill":
+        return bench_prefill(args, torch, pa)
     log(f"building workload {args.config}")
     b = build_workload(args.config)
     nbytes = algorithmic_bytes(b)
