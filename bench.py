@@ -397,43 +397,9 @@ def bench_prefill(args, torch, pa) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama7b")
-    ap.add_argument("--op", default="decode", choices=("decode", "copy_blocks", "prefill"),
-                    help="decode: the decode step (default); copy_blocks: the block-copy kernel; "
-                         "prefill: the prompt stage (multi-token write + causal prefill)")
-    ap.add_argument("--partition-size", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--eager", action="store_true",
-                    help="time eager launches only (no HIP graph replay)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run the 1 GiB copy kernel --steps times (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
-              f"single-GPU and shards by sequence or KV head without communication.", file=sys.stderr)
-        return 2
-
-    import torch
-    import paged_kv_cache_132_amd as pa
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    pa.load()
-    if args.copy_calibration:
-        return copy_calibration(torch, args.steps)
-    if args.op == "copy_blocks":
-        return bench_copy_blocks(args, torch, pa)
-    if args.op == "prefill":
-        return bench_prefill(args, torch, pa)
-    log(f"building workload {args.config}")
-    b = build_workload(args.config)
+def run_decode(args, torch, pa, b) -> dict:
+    """Time the decode step (write + attention + merge) on batch b; the
+    result dict of the JSON line, without the CPU baseline."""
     nbytes = algorithmic_bytes(b)
     pool_bytes = b.num_blocks * 2 * b.block_size * b.num_kv_heads * b.head_dim * ELEM[b.kv_dtype]
     copies = max(2, math.ceil((2 << 30) / pool_bytes))
@@ -531,7 +497,7 @@ def main() -> int:
         f"pa_decode call {call_us:.1f} us; write {write_ms.mean() * 1e3:.1f} us; eager step "
         f"{eager_ms_step * 1e3:.1f} us; graph step "
         f"{'-' if graph_ms_step is None else f'{graph_ms_step * 1e3:.1f}'} us")
-    traffic = counter_traffic(args.config, partition)
+    traffic = counter_traffic(b.name, partition)
     achievable = stream_read_gbs(torch)
     log(f"streaming-read kernel reaches {achievable:.0f} GB/s on this device")
 
@@ -580,6 +546,92 @@ def main() -> int:
     }
     if b.notes.get("prefix_blocks"):
         res["unique_kv_gbs"] = round(nbytes["unique_kv_blocks"] / (attn_us * 1e-6) / 1e9, 1)
+    return res
+
+
+def bench_block_sizes(args, torch, pa) -> int:
+    """The block-size sweep of [nano-vllm blog §5.1] / [CANN notes §5.1]: the
+    7B decode batch (same lengths) at block sizes 8, 16 and 32, each with the
+    allocator's usage counters ([CANN notes §5.4]) and its last-block waste."""
+    from workloads import make_llama7b
+
+    sweep = {}
+    for bs in (8, 16, 32):
+        b = make_llama7b(block_size=bs)
+        r = run_decode(args, torch, pa, b)
+        sweep[bs] = {
+            "attention_kernel_us": r["decode_attention_kernel_us"],
+            "decode_call_us": r["decode_call_us"],
+            "ms_per_step": r["ms_per_step"],
+            "kv_gbs": r["roofline"]["achieved"],
+            "step_gbs": r["value"],
+            "decode_tokens_per_s_per_layer": r["decode_tokens_per_s_per_layer"],
+            "partition_size": r["config"]["partition_size"],
+            "usage": b.manager.usage(b.tables, b.context_lens),
+        }
+        log(f"block size {bs}: attention {r['decode_attention_kernel_us']:.1f} us, "
+            f"step {r['ms_per_step'] * 1e3:.1f} us, slot utilisation "
+            f"{sweep[bs]['usage']['slot_utilisation']:.4f}")
+        del b
+        torch.cuda.empty_cache()
+    base = sweep[16]
+    for bs in sweep:
+        sweep[bs]["step_throughput_vs_bs16"] = round(base["ms_per_step"] / sweep[bs]["ms_per_step"], 4)
+    res = {
+        "metric": "paged decode KV-read GB/s vs block size (8/16/32), 1 GPU",
+        "value": base["step_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": base["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "llama7b block-size sweep", "block_sizes": [8, 16, 32], "value_at": 16},
+        "roofline": {"bound": "hbm", "achieved": base["kv_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(base["kv_gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
+        "sweep": sweep,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama7b")
+    ap.add_argument("--op", default="decode", choices=("decode", "copy_blocks", "prefill", "block_sizes"),
+                    help="decode: the decode step (default); copy_blocks: the block-copy kernel; "
+                         "prefill: the prompt stage (multi-token write + causal prefill); "
+                         "block_sizes: the decode step at block sizes 8, 16, 32")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 1 GiB copy kernel --steps times (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
+              f"single-GPU and shards by sequence or KV head without communication.", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_132_amd as pa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pa.load()
+    if args.copy_calibration:
+        return copy_calibration(torch, args.steps)
+    if args.op == "copy_blocks":
+        return bench_copy_blocks(args, torch, pa)
+    if args.op == "prefill":
+        return bench_prefill(args, torch, pa)
+    if args.op == "block_sizes":
+        return bench_block_sizes(args, torch, pa)
+    log(f"building workload {args.config}")
+    b = build_workload(args.config)
+    res = run_decode(args, torch, pa, b)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)

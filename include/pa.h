@@ -48,7 +48,7 @@
  * max_blocks_per_seq * block_size -- the results are then meaningless, but
  * memory outside the arguments is never touched.
  *
- * Supported: head_dim 64 or 128; block_size 16 or 32; num_heads a multiple
+ * Supported: head_dim 64 or 128; block_size 8, 16 or 32; num_heads a multiple
  * of num_kv_heads with num_heads / num_kv_heads in {1, 2, 4, 8} (query head h
  * reads KV head h / (num_heads / num_kv_heads)); (query, kv) dtypes
  * (F16, F16), (BF16, BF16) and (BF16, FP8_E4M3).  Other combinations return

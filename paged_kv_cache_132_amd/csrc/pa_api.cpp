@@ -30,10 +30,11 @@ constexpr int kMaxPartition = 1 << 20;
 
 }  // namespace
 
-DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size) {
+DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size, int block_size) {
     DecodeGeometry g;
-    // fp8 KV is only paired with a bf16 query (checked with the arguments)
-    g.mfma = gqa_mfma_supported(PA_BF16, kv_dtype, head_dim, group_size);
+    // fp8 KV is only paired with a bf16 query (checked with the arguments);
+    // the matrix-core kernel walks 16-token halves that must not cross a block
+    g.mfma = block_size >= 16 && gqa_mfma_supported(PA_BF16, kv_dtype, head_dim, group_size);
     g.kv_bytes = kv_dtype == PA_FP8_E4M3 ? 1 : 2;
     g.row_lanes = head_dim * g.kv_bytes / 16;
     g.rows = g.mfma ? kDecodeWaves : 64 / g.row_lanes;
@@ -56,7 +57,7 @@ pa_status check_decode_args(const void* out, const void* query, pa_dtype q_dtype
     const int group = num_heads / num_kv_heads;
     if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
     const bool combo = (q_dtype == PA_F16 && kv_dtype == PA_F16) ||
                        (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3);
@@ -87,7 +88,7 @@ bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
     if (partition_size != 0 && (partition_size % block_size != 0 || partition_size > kMaxPartition))
         return false;
     DecodePlan p;
-    p.geo = decode_geometry(head_dim, kv_dtype, num_heads / num_kv_heads);
+    p.geo = decode_geometry(head_dim, kv_dtype, num_heads / num_kv_heads, block_size);
     p.groups = (num_kv_heads + p.geo.rows - 1) / p.geo.rows;
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
     int part = partition_size;
@@ -145,7 +146,7 @@ static pa_status cache_write_rows(void* kv_pool, pa_dtype kv_dtype, const void* 
         max_blocks_per_seq <= 0 || num_blocks <= 0)
         return PA_ERR_BAD_SHAPE;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
     const bool combo = (src_dtype == kv_dtype && src_dtype != PA_FP8_E4M3) ||
                        (kv_dtype == PA_FP8_E4M3 && (src_dtype == PA_BF16 || src_dtype == PA_F16));
     if (!combo) return PA_ERR_UNSUPPORTED;

@@ -31,7 +31,7 @@ struct DecodeGeometry {
 };
 
 bool gqa_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int group_size);
-DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size);
+DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size, int block_size);
 
 // Host-side launch plan of one pa_decode call.
 struct DecodePlan {

@@ -27,6 +27,10 @@
 //   soft  online softmax in the exp2 domain: masked keys (after the row's
 //         position) get weight 0; probabilities are rounded to the MFMA
 //         input type once and the running sum uses the rounded values.
+//         With bf16 K/V the probability is split into a bf16 part and a bf16
+//         remainder and PV runs on both: one bf16 rounding (2^-9 relative)
+//         of a peaked softmax would otherwise move an output by up to
+//         2^-9 x the spread of the V values it weights.
 //   PV    A = P is the lane's own 8 probabilities (k-slot j = key 4q+j for
 //         j < 4, 16+4q+j-4 otherwise); B = V^T read back from LDS at the
 //         same key order; head_dim/16 MFMAs accumulate O[row][d] in fp32.
@@ -122,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     constexpr int VS = kKeys + 4;                       // LDS V^T row stride (elements)
     constexpr int KSTEPS = D / 32;
     constexpr int DT = D / 16;
+    constexpr bool SPLIT = QT == PA_BF16 && KVT == PA_BF16;   // P = bf16 part + bf16 remainder
 
     __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeys * KS];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VS];
@@ -257,12 +262,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         mx = fmaxf(mx, shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);              // finite: key 0 precedes every query
         const float alpha = fast_exp2(m_run - m_new);
-        uint16_t pb[8];
+        uint16_t pb[8], pl[8];
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pb[e] = M::round(sc[e] == -INFINITY ? 0.f : fast_exp2(sc[e] - m_new));
+            const float pe = sc[e] == -INFINITY ? 0.f : fast_exp2(sc[e] - m_new);
+            pb[e] = M::round(pe);
             psum += M::widen(pb[e]);
+            if constexpr (SPLIT) {
+                pl[e] = M::round(pe - M::widen(pb[e]));        // the difference is exact in fp32
+                psum += M::widen(pl[e]);
+            }
         }
         l_lane = l_lane * alpha + psum;
         m_run = m_new;
@@ -277,10 +287,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             }
         }
         // O += P V
-        const Vec pop = __builtin_bit_cast(Vec, make_uint4((uint32_t)pb[0] | ((uint32_t)pb[1] << 16),
-                                                           (uint32_t)pb[2] | ((uint32_t)pb[3] << 16),
-                                                           (uint32_t)pb[4] | ((uint32_t)pb[5] << 16),
-                                                           (uint32_t)pb[6] | ((uint32_t)pb[7] << 16)));
+        auto pack8 = [](const uint16_t (&v)[8]) {
+            return __builtin_bit_cast(Vec, make_uint4((uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                                                      (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+                                                      (uint32_t)v[4] | ((uint32_t)v[5] << 16),
+                                                      (uint32_t)v[6] | ((uint32_t)v[7] << 16)));
+        };
+        const Vec pop = pack8(pb);
+        Vec pop_lo;
+        if constexpr (SPLIT) pop_lo = pack8(pl);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             const uint16_t* vrow = &s_vt[(16 * t + c) * VS + 4 * q];
@@ -288,6 +303,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
             const Vec vf = __builtin_bit_cast(Vec, make_uint4(lo[0], lo[1], hi[0], hi[1]));
             oacc[t] = M::run(pop, vf, oacc[t]);
+            if constexpr (SPLIT) oacc[t] = M::run(pop_lo, vf, oacc[t]);
         }
         __syncthreads();
     }

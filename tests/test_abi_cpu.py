@@ -78,7 +78,7 @@ def call_decode(lib, **kw):
     (dict(q_dtype=FP8, kv_dtype=FP8), UNSUP),
     (dict(head_dim=96), UNSUP),
     (dict(head_dim=256), UNSUP),
-    (dict(block_size=8), UNSUP),
+    (dict(block_size=4), UNSUP),
     (dict(block_size=64), UNSUP),
     (dict(num_heads=12, num_kv_heads=8), SHAPE),
     (dict(num_heads=48, num_kv_heads=3), UNSUP),
@@ -206,7 +206,7 @@ def call_write_tokens(lib, **kw):
     (dict(cu_seqlens=FAKE + 4), MISAL),
     (dict(num_tokens=-1), SHAPE),
     (dict(src_dtype=FP8), UNSUP),
-    (dict(block_size=8), UNSUP),
+    (dict(block_size=64), UNSUP),
 ])
 def test_write_tokens_rejects_bad_arguments(lib, kw, status):
     assert call_write_tokens(lib, **kw) == status

@@ -78,6 +78,9 @@ SMALL_CASES = {
     "gqa2_fp8_d128_bs32": ([33, 1, 95, 288], 16, 8, 128, 32, "bf16", "fp8_e4m3"),
     "gqa4_fp8_d128_many_heads": ([17, 48, 500], 64, 16, 128, 16, "bf16", "fp8_e4m3"),
     "gqa4_fp8_d128_partial_wave_group": ([70, 300], 24, 6, 128, 16, "bf16", "fp8_e4m3"),
+    "mha_f16_d128_bs8": ([1, 7, 8, 9, 100, 301], 16, 16, 128, 8, "f16", "f16"),
+    "gqa2_bf16_d64_bs8": ([3, 50, 77, 130], 8, 4, 64, 8, "bf16", "bf16"),
+    "gqa4_fp8_d128_bs8": ([16, 100, 333, 1], 32, 8, 128, 8, "bf16", "fp8_e4m3"),
 }
 
 
@@ -85,7 +88,7 @@ SMALL_CASES = {
 def test_small_case(name):
     lens, hq, hkv, d, bs, qd, kvd = SMALL_CASES[name]
     b = make_custom(name, 100 + sorted(SMALL_CASES).index(name), lens, hq, hkv, d, bs, qd, kvd)
-    _run_case(b, partition_sizes=(0, bs, 2 * bs, 64 if bs == 16 else 96, b.max_blocks_per_seq * bs))
+    _run_case(b, partition_sizes=(0, bs, 2 * bs, 64 if bs <= 16 else 96, b.max_blocks_per_seq * bs))
 
 
 def test_zero_and_one_token_sequences():
@@ -103,7 +106,7 @@ def test_zero_and_one_token_sequences():
 # ---------------------------------------------------------------------------
 # addressing: one-hot probe and physical-block permutation
 
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32])
 def test_one_hot_probe_reads_the_addressed_slot(bs):
     """q = 16 e_0 and only the probe token has K[.,0] = 40: its weight exceeds
     every other by e^50, so the output is that token's V row bit for bit."""
@@ -129,7 +132,7 @@ def test_one_hot_probe_reads_the_addressed_slot(bs):
             assert np.array_equal(got[s], oracle.to_f64(pool_u[blk, 1, off], "f16")), (s, t_rel)
 
 
-@pytest.mark.parametrize("hq,hkv,bs", [(32, 8, 16), (32, 8, 32), (8, 8, 16)])
+@pytest.mark.parametrize("hq,hkv,bs", [(32, 8, 16), (32, 8, 32), (8, 8, 16), (32, 8, 8)])
 def test_fp8_one_hot_probe_reads_every_code(hq, hkv, bs):
     """fp8 KV: the probed token's V row comes out exactly (v_scale 1), which
     checks the e4m3 decode of all 256 codes in the decode kernels."""
@@ -308,15 +311,15 @@ def test_fp8_write_bit_exact_with_special_values():
         assert np.array_equal(got, ref), (k_scale, v_scale, int((got != ref).sum()))
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_16bit_write_bit_exact(dtype):
-    b = make_custom("w16", 14, [1, 16, 17, 40, 5, 33, 64], 16, 16, 128, 32, dtype, dtype)
+@pytest.mark.parametrize("dtype,bs", [("f16", 32), ("bf16", 32), ("f16", 8)])
+def test_16bit_write_bit_exact(dtype, bs):
+    b = make_custom("w16", 14, [1, 16, 17, 40, 5, 33, 64], 16, 16, 128, bs, dtype, dtype)
     bt, lens = b.block_table_array(), b.context_lens
     pool = poison_unused(b.kv_pool, b.tables, lens - 1, dtype)
     pool_dev = dev_pool(pool, dtype)
     pa.cache_write(pool_dev, dev16(b.new_key[0], dtype), dev16(b.new_value[0], dtype), dev_i32(bt), dev_i32(lens))
     torch.cuda.synchronize()
-    ref = oracle.cache_write(pool, dtype, b.new_key[0], b.new_value[0], dtype, bt, lens, 32)
+    ref = oracle.cache_write(pool, dtype, b.new_key[0], b.new_value[0], dtype, bt, lens, bs)
     assert np.array_equal(host_bits(pool_dev).reshape(ref.shape), ref)
 
 

@@ -53,6 +53,8 @@ CASES = {
     "mqa_g8_fp8_d64": ([65, 64], [65, 1], 8, 1, 64, 16, "bf16", "fp8_e4m3"),
     "gqa4_fp8_bs32": ([200, 33], [200, 17], 32, 8, 128, 32, "bf16", "fp8_e4m3"),
     "empty_runs": ([50, 10, 7], [0, 10, 0], 4, 4, 128, 16, "f16", "f16"),
+    "prefix_bs8_f16": ([70, 20, 9], [30, 20, 1], 8, 8, 128, 8, "f16", "f16"),
+    "gqa4_fp8_bs8": ([100, 8], [60, 8], 16, 4, 64, 8, "bf16", "fp8_e4m3"),
 }
 
 
@@ -133,3 +135,18 @@ def test_packed_mixed_prompts_full_size_sampled():
             ref = oracle.paged_prefill(b.query[j:j + 1], "f16", want_pool, "f16", bt[s:s + 1],
                                        np.array([i + 1], dtype=np.int32), np.array([0, 1]), b.block_size, b.scale)
             assert_decode_close(got[j:j + 1], ref, b)
+
+
+@pytest.mark.parametrize("qd,kvd", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "fp8_e4m3")])
+def test_peaked_softmax_precision(qd, kvd):
+    """Softmax scale 0.5 instead of 1/sqrt(128): scores spread over tens of
+    units, so a few keys carry almost all the weight and rounding of the
+    probabilities is not averaged away.  The tolerance still holds."""
+    b = make_prefill("peaked", 73, [300, 129, 64], [120, 129, 64], 16, 4, 128, 16, qd, kvd)
+    b.scale = 0.5
+    pool = _start_pool(b)
+    dev, out = _gpu_prompt(b, pool)
+    want_pool = _oracle_pool(b, pool)
+    ref = oracle.paged_prefill(b.query, qd, want_pool, kvd, b.block_table_array(), b.context_lens,
+                               b.cu_seqlens, 16, b.scale, b.k_scale, b.v_scale)
+    assert_decode_close(oracle.to_f64(host_bits(out), qd), ref, b)

@@ -518,3 +518,35 @@ def test_planted_encoder_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "e4m3_encode", truncating)
     with pytest.raises(AssertionError):
         test_e4m3_fixture_values()
+
+
+# ---------------------------------------------------------------------------
+# allocator usage counters ([CANN notes §5.4]) and last-block waste
+# ([nano-vllm blog §5.1]: about block_size / 2 tokens per sequence)
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_last_block_waste_closed_form(bs):
+    """Lengths covering every residue mod block_size equally often waste
+    exactly (block_size - 1) / 2 slots per sequence on average, and the
+    slot utilisation is tokens / allocated slots."""
+    lens = list(range(1, 4 * bs + 1))                   # 4 full periods of residues
+    mgr = BlockManager(sum(blocks_for_tokens(L, bs) for L in lens) + 5, bs)
+    tables = []
+    for L in lens:
+        tab = []
+        mgr.grow_to(tab, L)
+        tables.append(tab)
+    u = mgr.usage(tables, lens)
+    assert u["waste_tokens_per_seq"] == (bs - 1) / 2
+    slots = sum(-(-L // bs) for L in lens) * bs
+    assert u["slot_utilisation"] == sum(lens) / slots
+    assert u["allocated_blocks"] == u["used_blocks"] == slots // bs
+    assert u["pool_blocks"] - u["allocated_blocks"] == 5
+
+
+def test_usage_counts_shared_blocks_once():
+    b = make_prefix_shared(num_seqs=16, seq_len=300, prefix_tokens=256)
+    u = b.manager.usage(b.tables, b.context_lens)
+    per_table = sum(len(t) for t in b.tables)
+    assert u["used_blocks"] < per_table                  # the shared prefix is counted once
+    assert u["used_blocks"] == u["allocated_blocks"]

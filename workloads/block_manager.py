@@ -102,6 +102,37 @@ class BlockManager:
         """A block may be written only while exactly one table references it."""
         return self.ref_count[block] == 1
 
+    def usage(self, tables: list[list[int]], lens) -> dict:
+        """Allocation counters of [CANN notes §5.4] and the internal
+        fragmentation of [nano-vllm blog §5.1] / [CANN notes §5.1]:
+
+          pool_blocks            blocks in the pool
+          allocated_blocks       blocks taken from the free list
+          used_blocks            distinct blocks holding at least one token
+          block_utilisation      used_blocks / allocated_blocks
+          slot_utilisation       tokens / (table blocks x block_size), per table
+          waste_tokens_per_seq   mean empty slots in a sequence's blocks (its
+                                 last block only; about block_size / 2)
+          mean_table_length      mean blocks per table"""
+        lens = [int(x) for x in lens]
+        used = set()
+        slots = 0
+        for tab, L in zip(tables, lens):
+            n = blocks_for_tokens(L, self.block_size)
+            used.update(int(b) for b in tab[:n])
+            slots += len(tab) * self.block_size
+        allocated = self.num_blocks - self.num_free
+        tokens = sum(lens)
+        return {
+            "pool_blocks": self.num_blocks,
+            "allocated_blocks": allocated,
+            "used_blocks": len(used),
+            "block_utilisation": len(used) / allocated if allocated else 0.0,
+            "slot_utilisation": tokens / slots if slots else 0.0,
+            "waste_tokens_per_seq": (slots - tokens) / len(lens) if lens else 0.0,
+            "mean_table_length": float(np.mean([len(t) for t in tables])) if tables else 0.0,
+        }
+
     def dump(self, tables: list[list[int]], lens: list[int]) -> str:
         """Debug view: each sequence's table with the refcount of every block."""
         lines = [f"free={self.num_free}/{self.num_blocks}"]

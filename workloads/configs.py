@@ -247,12 +247,16 @@ def make_tiny(seed: int = 1) -> PagedBatch:
                   num_blocks=64, appends=1)
 
 
-def make_llama7b(seed: int = 2, num_seqs: int = 32, min_len: int = 128, max_len: int = 2048) -> PagedBatch:
-    """LLaMA-2-7B single-layer decode: 32/32 heads, D 128, fp16, bs 16, U[128, 2048] lengths."""
-    return _build("llama7b", seed,
+def make_llama7b(seed: int = 2, num_seqs: int = 32, min_len: int = 128, max_len: int = 2048,
+                 block_size: int = 16) -> PagedBatch:
+    """LLaMA-2-7B single-layer decode: 32/32 heads, D 128, fp16, bs 16, U[128, 2048] lengths.
+
+    Other block sizes (the [nano-vllm blog §5.1] sweep) keep the same lengths."""
+    name = "llama7b" if block_size == 16 else f"llama7b_bs{block_size}"
+    return _build(name, seed,
                   lambda rng: rng.integers(min_len, max_len, size=num_seqs, endpoint=True),
-                  32, 32, 128, 16, "f16", "f16",
-                  max_blocks_per_seq=blocks_for_tokens(max_len, 16))
+                  32, 32, 128, block_size, "f16", "f16",
+                  max_blocks_per_seq=blocks_for_tokens(max_len, block_size))
 
 
 def make_mixed(seed: int = 3, block_size: int = 16, steps: int = 33) -> PagedBatch:
