@@ -72,7 +72,9 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = 4,         /* valid but not implemented combination          */
     PA_ERR_MISALIGNED = 5,          /* a pointer is not 16-byte aligned               */
     PA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes < pa_decode_workspace_size()   */
-    PA_ERR_HIP = 7                  /* the HIP runtime rejected a launch              */
+    PA_ERR_HIP = 7,                 /* the HIP runtime rejected a launch              */
+    PA_ERR_POOL_EXHAUSTED = 8,      /* block manager: not enough free blocks          */
+    PA_ERR_UNKNOWN_SEQUENCE = 9     /* block manager: no sequence with that id        */
 } pa_status;
 
 typedef enum pa_dtype {

@@ -24,6 +24,7 @@ from .fp8_e4m3 import (
     e4m3_quantise,
     MAX_FINITE,
 )
+from .block_manager_model import BlockManagerModel, ModelPoolExhausted
 from .block_ops import check_block_mapping, copy_blocks
 from .prefill import cache_write_tokens, packed_positions, paged_prefill
 from .paged_attention import (
@@ -39,7 +40,7 @@ from .paged_attention import (
 )
 
 __all__ = [
-    "check_block_mapping", "copy_blocks", "cache_write_tokens", "packed_positions", "paged_prefill",
+    "BlockManagerModel", "ModelPoolExhausted", "check_block_mapping", "copy_blocks", "cache_write_tokens", "packed_positions", "paged_prefill",
     "e4m3_value", "e4m3_decode_table", "e4m3_decode", "e4m3_encode", "e4m3_quantise",
     "MAX_FINITE", "to_f64", "kv_bytes_per_token", "slot_of", "num_blocks_of", "gather_kv",
     "paged_decode", "encode_for_cache", "cache_write", "encode_pool",

@@ -19,10 +19,14 @@ PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {
     0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
     4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_MISALIGNED", 6: "PA_ERR_WORKSPACE_TOO_SMALL", 7: "PA_ERR_HIP",
+    8: "PA_ERR_POOL_EXHAUSTED", 9: "PA_ERR_UNKNOWN_SEQUENCE",
 }
 EXPORTED = ("pa_cache_write", "pa_cache_write_tokens", "pa_copy_blocks", "pa_decode", "pa_decode_partials",
             "pa_decode_merge", "pa_decode_workspace_size", "pa_decode_partition_size", "pa_prefill",
-            "pa_status_string")
+            "pa_status_string",
+            "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
+            "pa_bm_free_sequence", "pa_bm_take_copies", "pa_bm_sequence_length", "pa_bm_block_table",
+            "pa_bm_ref_count", "pa_bm_stats_get")
 
 _lib = None
 _lock = threading.Lock()
@@ -57,6 +61,29 @@ def load() -> ctypes.CDLL:
         lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
         lib.pa_decode_partition_size.restype = i32
         lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
+        i64, u64, ip = ctypes.c_int64, ctypes.c_uint64, ctypes.POINTER(ctypes.c_int32)
+        lib.pa_bm_create.restype = vp
+        lib.pa_bm_create.argtypes = [i32, i32, u64, ip]
+        lib.pa_bm_destroy.restype = None
+        lib.pa_bm_destroy.argtypes = [vp]
+        lib.pa_bm_add_sequence.restype = ctypes.c_int
+        lib.pa_bm_add_sequence.argtypes = [vp, i64, ip, i32, ip]
+        lib.pa_bm_append_token.restype = ctypes.c_int
+        lib.pa_bm_append_token.argtypes = [vp, i64, i32]
+        lib.pa_bm_fork.restype = ctypes.c_int
+        lib.pa_bm_fork.argtypes = [vp, i64, i64]
+        lib.pa_bm_free_sequence.restype = ctypes.c_int
+        lib.pa_bm_free_sequence.argtypes = [vp, i64]
+        lib.pa_bm_take_copies.restype = i32
+        lib.pa_bm_take_copies.argtypes = [vp, ip, i32]
+        lib.pa_bm_sequence_length.restype = i32
+        lib.pa_bm_sequence_length.argtypes = [vp, i64]
+        lib.pa_bm_block_table.restype = i32
+        lib.pa_bm_block_table.argtypes = [vp, i64, ip, i32]
+        lib.pa_bm_ref_count.restype = i32
+        lib.pa_bm_ref_count.argtypes = [vp, i32]
+        lib.pa_bm_stats_get.restype = ctypes.c_int
+        lib.pa_bm_stats_get.argtypes = [vp, vp]
         lib.pa_status_string.restype = ctypes.c_char_p
         lib.pa_status_string.argtypes = [ctypes.c_int]
         _lib = lib

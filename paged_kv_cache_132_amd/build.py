@@ -19,8 +19,8 @@ INCLUDE = os.path.join(REPO, "include")
 LIB = os.path.join(PKG, "libpa.so")
 BENCH_LIB = os.path.join(PKG, "libpa_bench.so")
 
-SOURCES = ["pa_api.cpp", "cache_write.hip", "copy_blocks.hip", "decode.hip", "decode_gqa_mfma.hip",
-           "prefill.hip"]
+SOURCES = ["pa_api.cpp", "block_manager.cpp", "cache_write.hip", "copy_blocks.hip", "decode.hip",
+           "decode_gqa_mfma.hip", "prefill.hip"]
 BENCH_SOURCES = ["bench_util.hip"]
 
 

@@ -131,6 +131,8 @@ const char* pa_status_string(pa_status status) {
         case PA_ERR_MISALIGNED: return "PA_ERR_MISALIGNED";
         case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
         case PA_ERR_HIP: return "PA_ERR_HIP";
+        case PA_ERR_POOL_EXHAUSTED: return "PA_ERR_POOL_EXHAUSTED";
+        case PA_ERR_UNKNOWN_SEQUENCE: return "PA_ERR_UNKNOWN_SEQUENCE";
     }
     return "PA_ERR_UNKNOWN";
 }

@@ -14,7 +14,7 @@ import paged_kv_cache_132_amd as pa
 from paged_kv_cache_132_amd import _lib
 
 REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(REPO, "include", "pa.h")
+HEADERS = [os.path.join(REPO, "include", h) for h in ("pa.h", "pa_block_manager.h")]
 
 OK, NULLP, SHAPE, DTYPE, UNSUP, MISAL, WS, HIP = range(8)
 F16, BF16, FP8 = 0, 1, 2
@@ -22,9 +22,11 @@ FAKE = 0x10000          # aligned, never dereferenced
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
