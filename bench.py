@@ -1,10 +1,13 @@
 """Benchmark of the paged-decode hot path on one MI355X.
 
-One step = pa_cache_write (each sequence's newest token, t = len - 1) followed
-by pa_decode over the whole batch, with every input already resident in HBM.
-The KV pool is replicated R times (at least 2 GiB in all) and successive steps
-rotate through the copies, so each step reads its pool from HBM rather than
-from the 256 MB last-level cache.
+One step = the cache write of each sequence's newest token (t = len - 1) and
+the decode over the whole batch, with every input already resident in HBM:
+by default pa_decode_write_partials (the write fused into the attention
+pass) + pa_decode_merge; with --separate-write, pa_cache_write +
+pa_decode_partials + pa_decode_merge.  The KV pool is replicated R times
+(at least 2 GiB in all) and successive steps rotate through the copies, so
+each step reads its pool from HBM rather than from the 256 MB last-level
+cache.
 
 Steps run twice: eagerly, with HIP events around every launch (the per-kernel
 breakdown), and as replays of a HIP graph holding the same three launches
@@ -415,18 +418,25 @@ def run_decode(args, torch, pa, b) -> dict:
     out = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
 
+    fused = not args.separate_write and b.q_dtype == b.src_dtype
+
     def step(i, ev=None):
-        # one pass of the hot path: cache write, attention pass, split-K merge
-        # (pa_decode == pa_decode_partials + pa_decode_merge, timed apart)
+        # one pass of the hot path: cache write, attention pass, split-K merge.
+        # Fused (default): pa_decode_write_partials writes the newest token in
+        # the attention pass; otherwise pa_cache_write runs first.
         pool = dev["pools"][i % copies]
         dargs = (dev["q"], pool, dev["bt"], dev["lens"], b.scale, b.k_scale, b.v_scale)
         dkw = dict(out=out, workspace=ws, partition_size=args.partition_size)
         if ev is not None:
             ev[0].record(stream)
-        pa.cache_write(pool, dev["k"], dev["v"], dev["bt"], dev["lens"], b.k_scale, b.v_scale)
+        if not fused:
+            pa.cache_write(pool, dev["k"], dev["v"], dev["bt"], dev["lens"], b.k_scale, b.v_scale)
         if ev is not None:
             ev[1].record(stream)
-        pa.decode(*dargs, phase="partials", **dkw)
+        if fused:
+            pa.decode(*dargs, phase="partials", new_key=dev["k"], new_value=dev["v"], **dkw)
+        else:
+            pa.decode(*dargs, phase="partials", **dkw)
         if ev is not None:
             ev[2].record(stream)
         pa.decode(*dargs, phase="merge", **dkw)
@@ -489,12 +499,15 @@ def run_decode(args, torch, pa, b) -> dict:
     ms_step = graph_ms_step if graph_ms_step is not None else eager_ms_step
     attn_us = float(attn_ms.mean() * 1e3)
     call_us = float(call_ms.mean() * 1e3)
-    achieved = nbytes["decode"] / (attn_us * 1e-6) / 1e9
+    # the attention kernel's algorithmic bytes: the decode's, plus the write's when fused
+    attn_bytes = nbytes["decode"] + (nbytes["write"] if fused else 0)
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     step_bytes = nbytes["decode"] + nbytes["write"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"attention pass mean {attn_us:.1f} us (p10 {np.percentile(attn_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(attn_ms, 90) * 1e3:.1f}); merge {merge_ms.mean() * 1e3:.1f} us; "
-        f"pa_decode call {call_us:.1f} us; write {write_ms.mean() * 1e3:.1f} us; eager step "
+        f"pa_decode call {call_us:.1f} us; "
+        f"{'write fused' if fused else f'write {write_ms.mean() * 1e3:.1f} us'}; eager step "
         f"{eager_ms_step * 1e3:.1f} us; graph step "
         f"{'-' if graph_ms_step is None else f'{graph_ms_step * 1e3:.1f}'} us")
     traffic = counter_traffic(b.name, partition)
@@ -522,6 +535,8 @@ def run_decode(args, torch, pa, b) -> dict:
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_launch": "hip_graph" if graph_ms_step is not None else "eager",
+        "step_kernels": ("pa_decode_write_partials (cache write fused), pa_decode_merge" if fused else
+                         "pa_cache_write, pa_decode_partials, pa_decode_merge"),
         "eager_ms_per_step": round(eager_ms_step, 4),
         "decode_tokens_per_s_per_layer": round(b.num_seqs / (ms_step * 1e-3), 1),
         "decode_only_tokens_per_s_per_layer": round(b.num_seqs / (call_us * 1e-6), 1),
@@ -530,10 +545,10 @@ def run_decode(args, torch, pa, b) -> dict:
                                                    for q in (10, 50, 90)],
         "decode_merge_kernel_us": round(float(merge_ms.mean() * 1e3), 2),
         "decode_call_us": round(call_us, 2),
-        "decode_call_gbs": round(nbytes["decode"] / (call_us * 1e-6) / 1e9, 1),
+        "decode_call_gbs": round(attn_bytes / (call_us * 1e-6) / 1e9, 1),
         "hbm_read_achievable_gbs": round(achievable, 1),
         "decode_frac_of_achievable": round(achieved / achievable, 4),
-        "write_kernel_us": round(float(write_ms.mean() * 1e3), 2),
+        "write_kernel_us": round(float(write_ms.mean() * 1e3), 2) if not fused else None,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -668,6 +683,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--separate-write", action="store_true",
+                    help="run pa_cache_write as its own launch instead of fusing it into the attention pass")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -199,6 +199,40 @@ pa_status pa_decode_merge(void* out, const void* query, pa_dtype q_dtype,
                           void* stream);
 
 /*
+ * pa_decode_write, pa_decode_write_partials -- pa_cache_write and pa_decode
+ * (or pa_decode_partials) in one attention pass: the decode step of
+ * [CANN notes §4.3] (write the new token, then read every block) with one
+ * launch less.  The wave that reads the newest token (position L - 1) of a
+ * sequence and KV head first stores that token's K and V rows, exactly as
+ * pa_cache_write would (fp8: divided by k_scale / v_scale in IEEE fp32,
+ * e4m3 round-to-nearest-even, saturating), then reads them back.
+ *
+ *   key, value   [num_seqs, num_kv_heads, head_dim] of src_dtype, which must
+ *                equal q_dtype (else PA_ERR_UNSUPPORTED); 16-byte aligned.
+ *   The other arguments, the workspace and the results are those of
+ *   pa_decode / pa_decode_partials; pa_decode_merge completes
+ *   pa_decode_write_partials.  Sequences with context_lens[s] <= 0, or
+ *   longer than the table holds, are not written.  The pool afterwards is
+ *   bit for bit what pa_cache_write leaves.
+ */
+pa_status pa_decode_write(void* out, const void* query, pa_dtype q_dtype,
+                          const void* kv_pool, pa_dtype kv_dtype,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int32_t num_blocks, float scale, float k_scale, float v_scale,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          void* stream, const void* key, const void* value, pa_dtype src_dtype);
+pa_status pa_decode_write_partials(void* out, const void* query, pa_dtype q_dtype,
+                                   const void* kv_pool, pa_dtype kv_dtype,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, float scale, float k_scale, float v_scale,
+                                   int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                   void* stream, const void* key, const void* value, pa_dtype src_dtype);
+
+/*
  * pa_cache_write_tokens -- the prompt-stage write: put a packed run of new
  * tokens per sequence into the pool ([CANN notes §3.1] packed layout,
  * [CANN notes §4.2] prompt write into block offsets; [nano-vllm blog §4.3]

@@ -22,7 +22,7 @@ STATUS_NAMES = {
     8: "PA_ERR_POOL_EXHAUSTED", 9: "PA_ERR_UNKNOWN_SEQUENCE",
 }
 EXPORTED = ("pa_cache_write", "pa_cache_write_tokens", "pa_copy_blocks", "pa_decode", "pa_decode_partials",
-            "pa_decode_merge", "pa_decode_workspace_size", "pa_decode_partition_size", "pa_prefill",
+            "pa_decode_merge", "pa_decode_write", "pa_decode_write_partials", "pa_decode_workspace_size", "pa_decode_partition_size", "pa_prefill",
             "pa_status_string",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
             "pa_bm_free_sequence", "pa_bm_take_copies", "pa_bm_sequence_length", "pa_bm_block_table",
@@ -57,6 +57,9 @@ def load() -> ctypes.CDLL:
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, vp]
         lib.pa_copy_blocks.restype = ctypes.c_int
         lib.pa_copy_blocks.argtypes = [vp, i32, vp, i32, ctypes.c_int, i32, i32, i32, vp, i32, vp]
+        for fn in (lib.pa_decode_write, lib.pa_decode_write_partials):
+            fn.restype = ctypes.c_int
+            fn.argtypes = lib.pa_decode.argtypes + [vp, vp, ctypes.c_int]
         lib.pa_decode_workspace_size.restype = sz
         lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
         lib.pa_decode_partition_size.restype = i32
@@ -264,11 +267,15 @@ _default_ws: dict = {}
 def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tensor,
            context_lens: torch.Tensor, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
            out: torch.Tensor | None = None, workspace: torch.Tensor | Workspace | None = None,
-           partition_size: int = 0, stream=None, phase: str = "both") -> torch.Tensor:
+           partition_size: int = 0, stream=None, phase: str = "both",
+           new_key: torch.Tensor | None = None, new_value: torch.Tensor | None = None) -> torch.Tensor:
     """Paged decode attention; returns out [num_seqs, num_heads, head_dim] of query's dtype.
 
     phase: "both" (pa_decode), "partials" (pa_decode_partials) or "merge"
-    (pa_decode_merge, with the same arguments and workspace as the partials call)."""
+    (pa_decode_merge, with the same arguments and workspace as the partials call).
+    new_key / new_value ([num_seqs, num_kv_heads, head_dim], query dtype): write
+    each sequence's newest token in the same pass (pa_decode_write /
+    pa_decode_write_partials), as pa_cache_write would."""
     nb, bs, hkv, d = _pool_dims(kv_pool)
     if query.dim() != 3 or query.shape[2] != d or not query.is_contiguous():
         raise ValueError("query must be a contiguous [num_seqs, num_heads, head_dim] tensor")
@@ -286,10 +293,21 @@ def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tenso
         ws = workspace.get(need, query.device)
     else:
         ws = workspace
-    fn = {"both": load().pa_decode, "partials": load().pa_decode_partials, "merge": load().pa_decode_merge}[phase]
+    extra = ()
+    if new_key is None:
+        fn = {"both": load().pa_decode, "partials": load().pa_decode_partials,
+              "merge": load().pa_decode_merge}[phase]
+    else:
+        if phase == "merge":
+            raise ValueError("the fused write belongs to the attention pass, not the merge")
+        if new_value is None or new_key.shape != (B, hkv, d) or new_value.shape != new_key.shape \
+                or not (new_key.is_contiguous() and new_value.is_contiguous()) or new_value.dtype != new_key.dtype:
+            raise ValueError("new_key/new_value must be contiguous [num_seqs, num_kv_heads, head_dim] of one dtype")
+        fn = {"both": load().pa_decode_write, "partials": load().pa_decode_write_partials}[phase]
+        extra = (_ptr(new_key), _ptr(new_value), pa_dtype(new_key))
     st = fn(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), kvt,
-                          _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, mb, nb,
-                          float(scale), float(k_scale), float(v_scale), int(partition_size),
-                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+            _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, mb, nb,
+            float(scale), float(k_scale), float(v_scale), int(partition_size),
+            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream), *extra)
     _check(st, f"pa_decode ({phase})")
     return out

@@ -13,6 +13,7 @@
 
 #include <stdint.h>
 
+#include "kv_encode.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -20,38 +21,6 @@ namespace {
 
 constexpr int kWriteThreads = 256;
 constexpr int kElemsPerThread = 8;
-
-// 16-bit source element -> float32 (exact).
-template <int SRC>
-__device__ __forceinline__ float widen(uint32_t bits16) {
-    if constexpr (SRC == PA_BF16) {
-        return __uint_as_float(bits16 << 16);
-    } else {
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-    }
-}
-
-// float32 -> OCP e4m3 code: round to nearest, ties to even; magnitudes at or
-// beyond 448 saturate to 448; NaN keeps its sign and becomes 0x7F / 0xFF.
-__device__ __forceinline__ uint32_t e4m3_from_float(float y) {
-    const uint32_t bits = __float_as_uint(y);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const float a = fabsf(y);
-    if (a != a) return sign | 0x7Fu;
-    if (!(a < 448.0f)) return sign | 0x7Eu;
-    if (a < 0.015625f) {
-        // Subnormal range: multiples of 2^-9.  a * 512 is exact and < 8;
-        // rintf rounds half to even.  8 (= 2^-6) becomes the smallest normal.
-        return sign | (uint32_t)rintf(a * 512.0f);
-    }
-    // Normal range [2^-6, 448): keep 3 of the 23 mantissa bits, rounding the
-    // dropped 20 bits to nearest even; a carry bumps the exponent correctly.
-    uint32_t ab = __float_as_uint(a);
-    ab += 0x7FFFFu + ((ab >> 20) & 1u);
-    const uint32_t e = (ab >> 23) - 127u + 7u;   // 1 .. 15
-    const uint32_t m = (ab >> 20) & 7u;
-    return sign | (e << 3) | m;
-}
 
 template <int SRC, int KVT>
 __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a) {

@@ -41,6 +41,7 @@
 #include <stdint.h>
 
 #include "decode_common.h"
+#include "kv_encode.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -160,7 +161,7 @@ __device__ __forceinline__ void accumulate_v(float (&o)[EPL], float p, const uin
 template <int QT, int D, int NE>
 __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h, int d0, int n_part);
 
-template <int QT, int KVT, int D, int G>
+template <int QT, int KVT, int D, int G, bool WRITE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     constexpr int KVB = KVT == PA_FP8_E4M3 ? 1 : 2;
     constexpr int ROWL = D * KVB / 16;      // lanes per KV-head row
@@ -227,6 +228,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const uint32_t lane_off = (uint32_t)((g * D + j * EPL) * KVB);         // this lane's 16 bytes
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
     const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    // the fused write applies to lengths the table holds (as pa_cache_write)
+    const bool write_len = WRITE && a.context_lens[s] == L;
 
     float m[G], l[G], o[G][EPL];
 #pragma unroll
@@ -284,6 +287,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     // the caches.  Every other block is streamed with nontemporal loads.
     const int lb_first = t_begin >> shift;
     const int lb_last = (t_end - 1) >> shift;
+
+    // Fused cache write ([CANN notes §4.3]: write the new token, then read
+    // every block).  The newest token sits in the last partition, in the
+    // segment and chunk found below.  The wave that will load that chunk
+    // stores the token's encoded rows before it issues any load, each lane
+    // the 16 bytes it later reads itself: one lane's global accesses to one
+    // address take effect in program order, so the loads see the new bytes
+    // with no wait on the stores.
+    if (WRITE && write_len && t_end == L) {
+        const int t_new = L - 1;
+        const int sg = lb_first + (((t_new >> shift) - lb_first) & ~63);
+        const int cn = (t_new - max(t_begin, sg << shift)) / TPC;
+        const int blk = bt_row[t_new >> shift];
+        if (cn % NW == wave && row_ok && blk >= 0 && blk < a.num_blocks) {
+            const int64_t src = ((int64_t)s * a.num_kv_heads + g) * D + j * EPL;
+            const int64_t row = ((int64_t)blk * 2 << shift) + (t_new & (a.block_size - 1));
+            uint8_t* kdst = const_cast<uint8_t*>(pool) + row * row_bytes + lane_off;
+            *reinterpret_cast<uint4*>(kdst) =
+                encode_chunk16<QT, KVT>(static_cast<const uint16_t*>(a.new_key) + src, a.write_k_scale);
+            *reinterpret_cast<uint4*>(kdst + half_bytes) =
+                encode_chunk16<QT, KVT>(static_cast<const uint16_t*>(a.new_value) + src, a.write_v_scale);
+        }
+    }
     for (int seg0 = lb_first; seg0 <= lb_last; seg0 += 64) {
         const int seg_blocks = min(64, lb_last - seg0 + 1);
         const bool in_seg = lane < seg_blocks;
@@ -450,13 +476,16 @@ __global__ __launch_bounds__(kDecodeThreads) void merge_kernel(DecodeArgs a) {
 template <int QT, int KVT, int D>
 int launch_d(const DecodeArgs& a, const DecodePlan& plan, int group_size, hipStream_t st) {
     const dim3 grid((unsigned)plan.grid), block(kDecodeThreads);
+    void (*kernel)(DecodeArgs);
+    const bool w = a.new_key != nullptr;
     switch (group_size) {
-        case 1: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 1>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 2>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 4>), grid, block, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((decode_kernel<QT, KVT, D, 8>), grid, block, 0, st, a); break;
+        case 1: kernel = w ? decode_kernel<QT, KVT, D, 1, true> : decode_kernel<QT, KVT, D, 1, false>; break;
+        case 2: kernel = w ? decode_kernel<QT, KVT, D, 2, true> : decode_kernel<QT, KVT, D, 2, false>; break;
+        case 4: kernel = w ? decode_kernel<QT, KVT, D, 4, true> : decode_kernel<QT, KVT, D, 4, false>; break;
+        case 8: kernel = w ? decode_kernel<QT, KVT, D, 8, true> : decode_kernel<QT, KVT, D, 8, false>; break;
         default: return (int)hipErrorInvalidValue;
     }
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
     return (int)hipGetLastError();
 }
 

@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include "decode_common.h"
+#include "kv_encode.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -90,7 +91,7 @@ __device__ __forceinline__ float from_lane(float x, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
-template <int G>
+template <int G, bool WRITE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(DecodeArgs a) {
     static_assert(G == 2 || G == 4 || G == 8, "query heads per KV head");
     constexpr int NW = kDecodeWaves;
@@ -136,6 +137,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     const uint32_t lane_col = (uint32_t)(g * kD + 16 * (lane & 7));           // 16-byte chunk of the head's row
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
     const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    // the fused write applies to lengths the table holds (as pa_cache_write)
+    const bool write_len = WRITE && a.context_lens[s] == L;
 
     // LDS: this wave's K and V staging rows; transposed-read base address of this lane
     uint8_t* sk = s_kv[wave][0];
@@ -164,6 +167,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
         const int seg_t1 = min(t_end, (seg0 + seg_blocks) << shift);
         const int n_steps = (seg_t1 - seg_t0 + kStepTokens - 1) / kStepTokens;
 
+        // Fused cache write ([CANN notes §4.3]: write the new token, then read
+        // every block).  Before this segment's first load, the 8 lanes whose
+        // loads will cover the newest token store its encoded row, each lane
+        // the 16 bytes it later reads itself: one lane's global accesses to
+        // one address take effect in program order, so the loads see the new
+        // bytes with no wait on the stores.
+        if (write_len && L - 1 >= seg_t0 && L - 1 < seg_t1) {
+            const int t_new = L - 1;
+            const int blk = __builtin_amdgcn_readlane(my_blk, (t_new >> shift) - seg0);
+            if (blk >= 0 && blk < a.num_blocks && (lane >> 3) == (t_new & 7)) {
+                const int64_t row = ((int64_t)blk * 2 << shift) + (t_new & (a.block_size - 1));
+                uint8_t* kp = const_cast<uint8_t*>(pool) + row * row_bytes + lane_col;
+                const int64_t src = ((int64_t)s * a.num_kv_heads + g) * kD + 16 * (lane & 7);
+                *reinterpret_cast<uint4*>(kp) = encode_chunk16<PA_BF16, PA_FP8_E4M3>(
+                    static_cast<const uint16_t*>(a.new_key) + src, a.write_k_scale);
+                *reinterpret_cast<uint4*>(kp + half_bytes) = encode_chunk16<PA_BF16, PA_FP8_E4M3>(
+                    static_cast<const uint16_t*>(a.new_value) + src, a.write_v_scale);
+            }
+        }
         // Issue the K and V loads of step k.  Each load instruction reads 8
         // whole 128-byte head rows (8 lanes x 16 bytes per token): long runs
         // keep the request count per byte low.  Rows past the end are
@@ -190,6 +212,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
                 };
                 if ((shared >> ((th >> shift) - seg0)) & 1) load_half(cached_load);
                 else load_half(stream_load);
+
             }
         };
 
@@ -339,12 +362,15 @@ bool gqa_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int g
 int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)plan.grid), block(kDecodeThreads);
+    void (*kernel)(DecodeArgs);
+    const bool w = a.new_key != nullptr;
     switch (group_size) {
-        case 2: hipLaunchKernelGGL((decode_gqa_fp8_mfma_kernel<2>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((decode_gqa_fp8_mfma_kernel<4>), grid, block, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((decode_gqa_fp8_mfma_kernel<8>), grid, block, 0, st, a); break;
+        case 2: kernel = w ? decode_gqa_fp8_mfma_kernel<2, true> : decode_gqa_fp8_mfma_kernel<2, false>; break;
+        case 4: kernel = w ? decode_gqa_fp8_mfma_kernel<4, true> : decode_gqa_fp8_mfma_kernel<4, false>; break;
+        case 8: kernel = w ? decode_gqa_fp8_mfma_kernel<8, true> : decode_gqa_fp8_mfma_kernel<8, false>; break;
         default: return (int)hipErrorInvalidValue;
     }
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
     return (int)hipGetLastError();
 }
 

@@ -321,7 +321,8 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                     float scale, float k_scale, float v_scale, int32_t partition_size,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    const void* new_key = nullptr, const void* new_value = nullptr) {
     pa_status st = check_decode_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables,
                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                                      block_size, max_blocks_per_seq, num_blocks, scale, k_scale,
@@ -358,6 +359,10 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
     a.max_partitions = plan.max_partitions;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;
+    a.new_key = new_key;
+    a.new_value = new_value;
+    a.write_k_scale = k_scale;
+    a.write_v_scale = v_scale;
     const int err = launch_decode(a, plan, q_dtype, kv_dtype, head_dim, num_heads / num_kv_heads,
                                   phases, stream);
     return err == 0 ? PA_OK : PA_ERR_HIP;
@@ -377,5 +382,24 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
 pa_status pa_decode(PA_DECODE_PARAMS) { return decode_phases(kPhasePartials | kPhaseMerge, PA_DECODE_ARGS); }
 pa_status pa_decode_partials(PA_DECODE_PARAMS) { return decode_phases(kPhasePartials, PA_DECODE_ARGS); }
 pa_status pa_decode_merge(PA_DECODE_PARAMS) { return decode_phases(kPhaseMerge, PA_DECODE_ARGS); }
+
+// pa_decode with the newest tokens' K/V written by the attention pass itself
+static pa_status decode_write_phases(int phases, PA_DECODE_PARAMS, const void* key, const void* value,
+                                     pa_dtype src_dtype) {
+    if (!known_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
+    if (src_dtype != q_dtype) return PA_ERR_UNSUPPORTED;         // the fused write takes query-dtype rows
+    if (num_seqs > 0) {
+        if (!key || !value) return PA_ERR_NULL_POINTER;
+        if (!aligned16(key) || !aligned16(value)) return PA_ERR_MISALIGNED;
+    }
+    return decode_phases(phases, PA_DECODE_ARGS, key, value);
+}
+
+pa_status pa_decode_write(PA_DECODE_PARAMS, const void* key, const void* value, pa_dtype src_dtype) {
+    return decode_write_phases(kPhasePartials | kPhaseMerge, PA_DECODE_ARGS, key, value, src_dtype);
+}
+pa_status pa_decode_write_partials(PA_DECODE_PARAMS, const void* key, const void* value, pa_dtype src_dtype) {
+    return decode_write_phases(kPhasePartials, PA_DECODE_ARGS, key, value, src_dtype);
+}
 
 }  // extern "C"

@@ -68,6 +68,13 @@ struct DecodeArgs {
     int32_t groups, partition, max_partitions;
     float score_scale;      // scale * k_scale * log2(e): scores in the exp2 domain
     float v_scale;
+    // Fused cache write (null: none): the newest token's K/V rows
+    // [num_seqs, num_kv_heads, head_dim] in the query dtype, stored into the
+    // pool (fp8: divided by write_k_scale / write_v_scale, e4m3-encoded) by
+    // the wave that reads that token, before it reads it.
+    const void* new_key;
+    const void* new_value;
+    float write_k_scale, write_v_scale;
 };
 
 struct WriteArgs {

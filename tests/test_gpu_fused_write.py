@@ -1,0 +1,107 @@
+"""pa_decode_write (cache write fused into the attention pass) against the two
+separate calls and the oracle.
+
+The pool after the fused call must be bit for bit the oracle's cache write
+(and what pa_cache_write leaves); the output must be bit for bit that of
+pa_cache_write followed by pa_decode, and within tolerance of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_132_amd as pa
+from tests._gpu import assert_decode_close, dev16, dev_i32, dev_pool, host_bits, poison_unused, pool_of
+from workloads import make_custom
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (lens after the append, Hq, Hkv, D, bs, q_dtype, kv_dtype)
+    "mha_f16_bs16": ([1, 16, 17, 33, 300, 0], 32, 32, 128, 16, "f16", "f16"),
+    "mha_bf16_d64_bs32": ([5, 32, 33, 64, 257], 8, 8, 64, 32, "bf16", "bf16"),
+    "mha_f16_bs8": ([1, 8, 9, 100], 16, 16, 128, 8, "f16", "f16"),
+    "gqa4_f16_bs16": ([40, 200, 3], 32, 8, 128, 16, "f16", "f16"),
+    "gqa4_fp8_mfma_bs16": ([16, 17, 100, 333, 1, 64], 32, 8, 128, 16, "bf16", "fp8_e4m3"),
+    "gqa2_fp8_mfma_bs32": ([33, 1, 95, 288], 16, 8, 128, 32, "bf16", "fp8_e4m3"),
+    "gqa8_fp8_mfma_partial_group": ([40, 160], 16, 2, 128, 16, "bf16", "fp8_e4m3"),
+    "gqa4_fp8_vector_bs8": ([16, 100, 9], 32, 8, 128, 8, "bf16", "fp8_e4m3"),
+    "mha_fp8_vector_d64": ([40, 120, 2], 8, 8, 64, 16, "bf16", "fp8_e4m3"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("partition", [0, "bs", 64])
+def test_fused_write_equals_separate_calls(name, partition):
+    lens, hq, hkv, d, bs, qd, kvd = CASES[name]
+    b = make_custom(name, 200 + sorted(CASES).index(name), [max(L - 1, 0) for L in lens], hq, hkv, d, bs, qd, kvd,
+                    appends=1)
+    lens1 = np.array(lens, dtype=np.int32)
+    for tab, L in zip(b.tables, lens1):
+        b.manager.grow_to(tab, int(L))
+    bt_np = b.block_table_array()
+    pool_np = poison_unused(pool_of(b), b.tables, lens1 - 1, kvd)     # the new slots hold NaN until written
+    src = "bf16" if kvd == "fp8_e4m3" else kvd
+    k_raw, v_raw = b.new_key[0], b.new_value[0]
+    part = bs if partition == "bs" else partition
+    bt, lens_d = dev_i32(bt_np), dev_i32(lens1)
+    q = dev16(b.step_query[0], qd)
+    k, v = dev16(k_raw, src), dev16(v_raw, src)
+
+    pool_sep = dev_pool(pool_np, kvd)
+    pa.cache_write(pool_sep, k, v, bt, lens_d, b.k_scale, b.v_scale)
+    out_sep = pa.decode(q, pool_sep, bt, lens_d, b.scale, b.k_scale, b.v_scale, partition_size=part)
+    pool_fused = dev_pool(pool_np, kvd)
+    out_fused = pa.decode(q, pool_fused, bt, lens_d, b.scale, b.k_scale, b.v_scale, partition_size=part,
+                          new_key=k, new_value=v)
+    torch.cuda.synchronize()
+
+    want_pool = oracle.cache_write(pool_np, kvd, k_raw, v_raw, src, bt_np, lens1, bs, b.k_scale, b.v_scale)
+    assert np.array_equal(host_bits(pool_fused), want_pool)
+    assert np.array_equal(host_bits(pool_sep), want_pool)
+    assert torch.equal(out_fused.view(torch.int16), out_sep.view(torch.int16))
+    ref = oracle.paged_decode(b.step_query[0], qd, want_pool, kvd, bt_np, lens1, bs, b.scale, b.k_scale, b.v_scale)
+    assert_decode_close(oracle.to_f64(host_bits(out_fused), qd), ref, b)
+
+
+def test_fused_write_two_phase_and_graph():
+    """pa_decode_write_partials + pa_decode_merge equals pa_decode_write, and a
+    graph of the fused step replays to the same result every time."""
+    b = make_custom("fw2", 230, [299, 40, 1000], 32, 8, 128, 16, "bf16", "fp8_e4m3", appends=1)
+    lens1 = b.context_lens + 1
+    for tab, L in zip(b.tables, lens1):
+        b.manager.grow_to(tab, int(L))
+    bt, lens = dev_i32(b.block_table_array()), dev_i32(lens1)
+    q, k, v = dev16(b.step_query[0], "bf16"), dev16(b.new_key[0], "bf16"), dev16(b.new_value[0], "bf16")
+    pool0 = pool_of(b)
+    ws = torch.empty(pa.decode_workspace_size(3, 32, 8, 128, 16, b.max_blocks_per_seq, pa.PA_FP8_E4M3, 128),
+                     dtype=torch.uint8, device="cuda")
+    args = (bt, lens, b.scale, b.k_scale, b.v_scale)
+    pool_a = dev_pool(pool0, "fp8_e4m3")
+    one = pa.decode(q, pool_a, *args, partition_size=128, new_key=k, new_value=v)
+    pool_b = dev_pool(pool0, "fp8_e4m3")
+    two = torch.empty_like(one)
+
+    def step():
+        pa.decode(q, pool_b, *args, out=two, workspace=ws, partition_size=128, phase="partials",
+                  new_key=k, new_value=v)
+        pa.decode(q, pool_b, *args, out=two, workspace=ws, partition_size=128, phase="merge")
+
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    assert torch.equal(pool_a, pool_b)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(3):
+        two.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    assert torch.equal(pool_a, pool_b)
