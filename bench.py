@@ -62,24 +62,31 @@ def algorithmic_bytes(b) -> dict:
     return {"kv": kv, "decode": decode, "write": write, "unique_kv_blocks": unique_kv}
 
 
+# the sources the decode kernels and their launcher are built from
+DECODE_SOURCES = ("decode.hip", "decode_gqa_mfma.hip", "decode_common.h", "kv_encode.h", "pa_internal.h",
+                  "pa_api.cpp")
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(REPO, "paged_kv_cache_132_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in DECODE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def counter_traffic(config: str, partition: int):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; otherwise None."""
+def counter_traffic(config: str, partition: int, fused: bool):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, if
+    they were taken on the current decode sources, partition and step form
+    (cache write fused or separate); otherwise None."""
     path = os.path.join(REPO, "profiles", f"decode_{config}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash() or rec.get("partition") != partition:
+    if (rec.get("source_hash") != source_hash() or rec.get("partition") != partition
+            or rec.get("fused_write", False) != fused):
         return None
     return rec.get("attention_hbm_bytes_per_launch")
 
@@ -510,7 +517,7 @@ def run_decode(args, torch, pa, b) -> dict:
         f"{'write fused' if fused else f'write {write_ms.mean() * 1e3:.1f} us'}; eager step "
         f"{eager_ms_step * 1e3:.1f} us; graph step "
         f"{'-' if graph_ms_step is None else f'{graph_ms_step * 1e3:.1f}'} us")
-    traffic = counter_traffic(b.name, partition)
+    traffic = counter_traffic(b.name, partition, fused)
     achievable = stream_read_gbs(torch)
     log(f"streaming-read kernel reaches {achievable:.0f} GB/s on this device")
 
