@@ -8,17 +8,20 @@
 // head h -- attends to keys 0 .. L - n + i of its own sequence.
 //
 // Work decomposition
-//   Workgroup = (sequence, KV head g, tile of 64 rows); rows are the
+//   Workgroup = (sequence, KV head g, tile of 128 rows); rows are the
 //   (new token, query head) pairs of the G query heads that read KV head g,
 //   token-major, so one K/V tile in LDS serves G heads.  Wave w owns rows
-//   16w .. 16w+15 of the tile.  Tiles are dispatched last tile first: the
-//   latest queries see the most keys.
+//   32w .. 32w+31 of the tile as two 16-row MFMA blocks, so every K and V
+//   operand read from LDS feeds two MFMAs.  Tiles are dispatched last tile
+//   first: the latest queries see the most keys.  The sequence's block table
+//   is staged in LDS once (tables of up to 2048 blocks).
 //
 // Per 32-key tile (lane l: c = l % 16, q = l / 16):
 //   load  the 256 threads read the tile's K and V rows through the block
-//         table (16 bytes each) and stage them in LDS: K row-major, V
-//         transposed (head_dim-major); fp8 is widened to bf16 exactly.
-//         The next tile's loads are in flight while this one is computed.
+//         table (16 bytes each) and store them row-major into one of two LDS
+//         buffers (fp8 widened to bf16 exactly).  Tile kt + 1 is stored
+//         while tile kt is computed and the loads of tile kt + 2 go out
+//         right after: one barrier per tile.
 //   S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16}: A = K rows (lane: key c,
 //         head_dim 8q..8q+7 of each 32-wide step), B = the queries (lane:
 //         row c, the same head_dim positions, held in registers).  Two
@@ -32,8 +35,10 @@
 //         of a peaked softmax would otherwise move an output by up to
 //         2^-9 x the spread of the V values it weights.
 //   PV    A = P is the lane's own 8 probabilities (k-slot j = key 4q+j for
-//         j < 4, 16+4q+j-4 otherwise); B = V^T read back from LDS at the
-//         same key order; head_dim/16 MFMAs accumulate O[row][d] in fp32.
+//         j < 4, 16+4q+j-4 otherwise); B = V read from its row-major LDS
+//         copy with ds_read_tr16_b64 (two reads give a lane the 8 keys of one
+//         head_dim column in that k-slot order); head_dim/16 MFMAs per row
+//         block accumulate O[row][d] in fp32.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -49,10 +54,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;           // 4 waves
-constexpr int kRows = 64;               // (token, head) rows per workgroup
+constexpr int kRB = 2;                  // 16-row MFMA blocks per wave
+constexpr int kRows = 4 * 16 * kRB;     // (token, head) rows per workgroup
 constexpr int kKeys = 32;               // keys per tile
+constexpr int kMaxBt = 2048;            // block-table entries staged in LDS (longer tables are read in place)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -113,8 +122,8 @@ __device__ __forceinline__ void widen16_fp8(uint4 w, uint4& lo, uint4& hi) {
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-template <int QT, int KVT, int D, int G>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+template <int QT, int KVT, int D, int G, bool BT_LDS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
     using M = Mma<QT>;
     using Vec = typename M::Vec;
     constexpr int KB = KVT == PA_FP8_E4M3 ? 1 : 2;      // pool bytes per element
@@ -123,13 +132,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     constexpr int CHUNKS = kKeys * CPK;                 // chunks per K (or V) tile
     constexpr int U = (CHUNKS + kThreads - 1) / kThreads;
     constexpr int KS = D + 8;                           // LDS K row stride (elements)
-    constexpr int VS = kKeys + 4;                       // LDS V^T row stride (elements)
+    constexpr int VS = D + 16;                          // LDS V row stride: transposed reads of 4 rows x 16
+                                                        // columns fall in distinct banks
     constexpr int KSTEPS = D / 32;
     constexpr int DT = D / 16;
     constexpr bool SPLIT = QT == PA_BF16 && KVT == PA_BF16;   // P = bf16 part + bf16 remainder
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeys * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeys * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kKeys * VS];
+    __shared__ int32_t s_bt[BT_LDS ? kMaxBt : 1];
 
     // ---- work item ----------------------------------------------------------
     const int Hkv = a.num_kv_heads;
@@ -152,188 +163,235 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const int c = lane & 15;
     const int q = lane >> 4;
     const int Hq = a.num_heads;
-    const int row0 = tile * kRows;
+    const int row0 = tile * kRows + wave * 16 * kRB;     // this wave's first row
 
-    // this lane's row (as the B-operand column and for the softmax state)
-    const int r = min(row0 + 16 * wave + c, rows - 1);
-    const int pos = L - n + r / G;                       // query position
-    Vec qop[KSTEPS];
-    {
+    // this lane's rows (B-operand column c of each 16-row block)
+    int pos[kRB];                                        // query positions
+    Vec qop[kRB][KSTEPS];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+        const int r = min(row0 + 16 * rb + c, rows - 1);
+        pos[rb] = L - n + r / G;
         const uint16_t* qp = static_cast<const uint16_t*>(a.query) +
                              ((int64_t)(first + r / G) * Hq + g * G + r % G) * D + 8 * q;
 #pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) qop[k] = __builtin_bit_cast(Vec, *reinterpret_cast<const uint4*>(qp + 32 * k));
+        for (int k = 0; k < KSTEPS; ++k)
+            qop[rb][k] = __builtin_bit_cast(Vec, *reinterpret_cast<const uint4*>(qp + 32 * k));
     }
-    const int last_row = min(row0 + kRows, rows) - 1;
-    const int p_max = L - n + last_row / G;              // the latest query of the tile
+    const int last_row = min(tile * kRows + kRows, rows) - 1;
+    const int p_max = L - n + last_row / G;              // the latest query of the workgroup
     const int n_tiles = p_max / kKeys + 1;
 
-    // ---- K/V tile loads ---------------------------------------------------------
+    // ---- the sequence's block table, staged in LDS when tables are short ----
     const int shift = a.block_shift;
+    const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    if constexpr (BT_LDS) {
+        const int nblk = (L + a.block_size - 1) >> shift;      // <= max_blocks_per_seq <= kMaxBt
+        for (int i = tid; i < nblk; i += kThreads) s_bt[i] = bt_row[i];
+        __syncthreads();
+    }
+
+    // ---- K/V tile loads ---------------------------------------------------------
     const int64_t row_bytes = (int64_t)Hkv * D * KB;
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
-    const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
-    auto load_tile = [&](int kt, uint4 (&kr)[U], uint4 (&vr)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int ci = tid + kThreads * u;
-            if (ci < CHUNKS) {
-                const int key = ci / CPK;
-                const int ch = ci % CPK;
-                const int t = min(kt * kKeys + key, L - 1);   // keys past the last position are masked
-                int blk = bt_row[t >> shift];
-                blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-                const int64_t krow = ((int64_t)blk * 2 << shift) + (t & (a.block_size - 1));
-                const uint8_t* kp = pool + krow * row_bytes + (int64_t)(g * D + ch * EPC) * KB;
-                kr[u] = *reinterpret_cast<const uint4*>(kp);
-                vr[u] = *reinterpret_cast<const uint4*>(kp + (row_bytes << shift));
-            }
-        }
+    // Each thread moves U chunks of K and of V per tile (chunk tid + 256u).
+    // The loads are branch-free: where the tile has fewer chunks than
+    // threads, the spare threads re-read chunk 0 and store nothing.
+    static_assert(U <= 2, "at most two chunks per thread");
+    struct Tile {
+        uint4 k0, v0, k1, v1;
+    };
+    auto load_chunk = [&](int kt, int ci, uint4& kd, uint4& vd) {
+        ci = ci < CHUNKS ? ci : 0;
+        const int key = ci / CPK;
+        const int ch = ci % CPK;
+        const int t = min(kt * kKeys + key, L - 1);   // keys past the last position are masked
+        int blk;
+        if constexpr (BT_LDS) blk = s_bt[t >> shift];
+        else blk = bt_row[t >> shift];
+        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+        const int64_t krow = ((int64_t)blk * 2 << shift) + (t & (a.block_size - 1));
+        const uint8_t* kp = pool + krow * row_bytes + (int64_t)(g * D + ch * EPC) * KB;
+        kd = *reinterpret_cast<const uint4*>(kp);
+        vd = *reinterpret_cast<const uint4*>(kp + (row_bytes << shift));
+    };
+    auto load_tile = [&](int kt) {
+        Tile r;
+        load_chunk(kt, tid, r.k0, r.v0);
+        if constexpr (U > 1) load_chunk(kt, tid + kThreads, r.k1, r.v1);
+        return r;
     };
 
-    auto store_tile = [&](const uint4 (&kr)[U], const uint4 (&vr)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int ci = tid + kThreads * u;
-            if (ci < CHUNKS) {
-                const int key = ci / CPK;
-                const int d0 = (ci % CPK) * EPC;
-                uint4 k16[2], v16[2];
-                if constexpr (KVT == PA_FP8_E4M3) {
-                    widen16_fp8(kr[u], k16[0], k16[1]);
-                    widen16_fp8(vr[u], v16[0], v16[1]);
-                } else {
-                    k16[0] = kr[u];
-                    v16[0] = vr[u];
-                }
-#pragma unroll
-                for (int h = 0; h < EPC / 8; ++h) {
-                    *reinterpret_cast<uint4*>(&s_k[key * KS + d0 + 8 * h]) = k16[h];
-                    const uint32_t w[4] = {v16[h].x, v16[h].y, v16[h].z, v16[h].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        s_vt[(d0 + 8 * h + e) * VS + key] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-                }
-            }
+    // K and V both row-major in LDS (fp8 widened to bf16 exactly)
+    auto store_chunk = [&](int buf, int ci, uint4 kc, uint4 vc) {
+        if (CHUNKS % kThreads != 0 && ci >= CHUNKS) return;
+        const int key = ci / CPK;
+        const int d0 = (ci % CPK) * EPC;
+        if constexpr (KVT == PA_FP8_E4M3) {
+            uint4 klo, khi, vlo, vhi;
+            widen16_fp8(kc, klo, khi);
+            widen16_fp8(vc, vlo, vhi);
+            *reinterpret_cast<uint4*>(&s_k[buf][key * KS + d0]) = klo;
+            *reinterpret_cast<uint4*>(&s_k[buf][key * KS + d0 + 8]) = khi;
+            *reinterpret_cast<uint4*>(&s_v[buf][key * VS + d0]) = vlo;
+            *reinterpret_cast<uint4*>(&s_v[buf][key * VS + d0 + 8]) = vhi;
+        } else {
+            *reinterpret_cast<uint4*>(&s_k[buf][key * KS + d0]) = kc;
+            *reinterpret_cast<uint4*>(&s_v[buf][key * VS + d0]) = vc;
         }
     };
+    auto store_tile = [&](int buf, const Tile& tl) {
+        store_chunk(buf, tid, tl.k0, tl.v0);
+        if constexpr (U > 1) store_chunk(buf, tid + kThreads, tl.k1, tl.v1);
+    };
 
-    // ---- main loop --------------------------------------------------------------
-    float m_run = -INFINITY;   // running max of row c (same in the 4 lanes of the row)
-    float l_lane = 0.f;        // this lane's share of row c's running sum
-    f32x4 oacc[DT];
+    // ---- per-tile math -------------------------------------------------------------
+    float m_run[kRB], l_lane[kRB];   // running max of row c (same in the row's 4 lanes); lane share of the sum
+    f32x4 oacc[kRB][DT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < kRB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_lane[rb] = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) oacc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    uint4 kr[U], vr[U];
-    load_tile(0, kr, vr);
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        store_tile(kr, vr);
-        __syncthreads();
-        if (kt + 1 < n_tiles) load_tile(kt + 1, kr, vr);
-
-        // S^T = K Q^T for the tile's two 16-key halves
-        f32x4 sacc[2];
+    auto compute = [&](int kt, int buf) {
+        const uint16_t* sk = s_k[buf];
+        const uint16_t* sv = s_v[buf];
+        // S^T = K Q^T for the tile's two 16-key halves; each K operand serves both row blocks
+        f32x4 sacc[kRB][2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) sacc[rb][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < KSTEPS; ++k) {
-                const Vec kf = __builtin_bit_cast(Vec, *reinterpret_cast<const uint4*>(&s_k[(16 * u + c) * KS + 32 * k + 8 * q]));
-                acc = M::run(kf, qop[k], acc);
-            }
-            sacc[u] = acc;
-        }
-        // online softmax (lane: keys 4q+i and 16+4q+i of row c)
-        float sc[8];
-        float mx = -INFINITY;
+                const Vec kf = __builtin_bit_cast(Vec, *reinterpret_cast<const uint4*>(&sk[(16 * u + c) * KS + 32 * k + 8 * q]));
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kt * kKeys + 16 * u + 4 * q + i;
-                const float v = key <= pos ? sacc[u][i] * a.score_scale : -INFINITY;
-                sc[4 * u + i] = v;
-                mx = fmaxf(mx, v);
+                for (int rb = 0; rb < kRB; ++rb) sacc[rb][u] = M::run(kf, qop[rb][k], sacc[rb][u]);
             }
         }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);              // finite: key 0 precedes every query
-        const float alpha = fast_exp2(m_run - m_new);
-        uint16_t pb[8], pl[8];
-        float psum = 0.f;
+        // online softmax (lane: keys 4q+i and 16+4q+i of row c of each block)
+        Vec pop[kRB], pop_lo[kRB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pe = sc[e] == -INFINITY ? 0.f : fast_exp2(sc[e] - m_new);
-            pb[e] = M::round(pe);
-            psum += M::widen(pb[e]);
-            if constexpr (SPLIT) {
-                pl[e] = M::round(pe - M::widen(pb[e]));        // the difference is exact in fp32
-                psum += M::widen(pl[e]);
+        for (int rb = 0; rb < kRB; ++rb) {
+            float sc[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = kt * kKeys + 16 * u + 4 * q + i;
+                    const float v = key <= pos[rb] ? sacc[rb][u][i] * a.score_scale : -INFINITY;
+                    sc[4 * u + i] = v;
+                    mx = fmaxf(mx, v);
+                }
             }
-        }
-        l_lane = l_lane * alpha + psum;
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-            float ar[4];
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[rb], mx);          // finite: key 0 precedes every query
+            const float alpha = fast_exp2(m_run[rb] - m_new);
+            uint32_t pw[4] = {0u, 0u, 0u, 0u}, plw[4] = {0u, 0u, 0u, 0u};   // packed probabilities
+            float psum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ar[i] = from_lane(alpha, 4 * q + i);
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) oacc[t][i] *= ar[i];
+            for (int e = 0; e < 8; ++e) {
+                const float pe = sc[e] == -INFINITY ? 0.f : fast_exp2(sc[e] - m_new);
+                const uint16_t pb = M::round(pe);
+                psum += M::widen(pb);
+                pw[e >> 1] |= (uint32_t)pb << (16 * (e & 1));
+                if constexpr (SPLIT) {
+                    const uint16_t pl = M::round(pe - M::widen(pb));   // the difference is exact in fp32
+                    psum += M::widen(pl);
+                    plw[e >> 1] |= (uint32_t)pl << (16 * (e & 1));
+                }
             }
+            l_lane[rb] = l_lane[rb] * alpha + psum;
+            m_run[rb] = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+                float ar[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ar[i] = from_lane(alpha, 4 * q + i);
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oacc[rb][t][i] *= ar[i];
+                }
+            }
+            pop[rb] = __builtin_bit_cast(Vec, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+            if constexpr (SPLIT) pop_lo[rb] = __builtin_bit_cast(Vec, make_uint4(plw[0], plw[1], plw[2], plw[3]));
         }
-        // O += P V
-        auto pack8 = [](const uint16_t (&v)[8]) {
-            return __builtin_bit_cast(Vec, make_uint4((uint32_t)v[0] | ((uint32_t)v[1] << 16),
-                                                      (uint32_t)v[2] | ((uint32_t)v[3] << 16),
-                                                      (uint32_t)v[4] | ((uint32_t)v[5] << 16),
-                                                      (uint32_t)v[6] | ((uint32_t)v[7] << 16)));
-        };
-        const Vec pop = pack8(pb);
-        Vec pop_lo;
-        if constexpr (SPLIT) pop_lo = pack8(pl);
+        // O += P V.  B operand: lane (n, q) needs V[key][16t + n] for its 8
+        // k-slot keys 4q..4q+3 and 16+4q..16+4q+3.  ds_read_tr16_b64 gives
+        // lane i of a 16-lane group element (i % 4) of the 8 bytes addressed
+        // by lane 4j + (i % 16) / 4 as its element j, so lane 4j + m of the
+        // group addresses V[4q + j][16t + 4m] (and the same 16 keys on).
+        const int tr_key = 4 * q + (c >> 2);
+        const int tr_col = 4 * (c & 3);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-            const uint16_t* vrow = &s_vt[(16 * t + c) * VS + 4 * q];
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-            const Vec vf = __builtin_bit_cast(Vec, make_uint4(lo[0], lo[1], hi[0], hi[1]));
-            oacc[t] = M::run(pop, vf, oacc[t]);
-            if constexpr (SPLIT) oacc[t] = M::run(pop_lo, vf, oacc[t]);
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(&sv[tr_key * VS + 16 * t + tr_col]));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(&sv[(16 + tr_key) * VS + 16 * t + tr_col]));
+            const Vec vf = __builtin_bit_cast(Vec, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) {
+                oacc[rb][t] = M::run(pop[rb], vf, oacc[rb][t]);
+                if constexpr (SPLIT) oacc[rb][t] = M::run(pop_lo[rb], vf, oacc[rb][t]);
+            }
+        }
+    };
+
+    // ---- main loop: two LDS buffers --------------------------------------------
+    // Iteration kt computes tile kt from buffer kt & 1 while the loads of tile
+    // kt + 1, issued one iteration earlier, are in flight; it then stores them
+    // into the other buffer and issues the loads of tile kt + 2.  One barrier
+    // per tile.
+    Tile tl = load_tile(0);
+    store_tile(0, tl);
+    if (n_tiles > 1) tl = load_tile(1);
+    __syncthreads();
+    for (int kt = 0; kt < n_tiles; ++kt) {
+        compute(kt, kt & 1);
+        if (kt + 1 < n_tiles) {
+            store_tile((kt + 1) & 1, tl);
+            if (kt + 2 < n_tiles) tl = load_tile(kt + 2);
         }
         __syncthreads();
     }
 
     // ---- finish: row sums, normalise, store ----------------------------------
-    l_lane += shfl_xor(l_lane, 16);
-    l_lane += shfl_xor(l_lane, 32);
-    float lr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lr[i] = from_lane(l_lane, 4 * q + i);
     uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int R = row0 + 16 * wave + 4 * q + i;
-        if (R >= rows) continue;
-        const float inv = a.v_scale / lr[i];
-        uint16_t* dst = out + ((int64_t)(first + R / G) * Hq + g * G + R % G) * D + c;
+    for (int rb = 0; rb < kRB; ++rb) {
+        float lsum = l_lane[rb];
+        lsum += shfl_xor(lsum, 16);
+        lsum += shfl_xor(lsum, 32);
+        float lr[4];
 #pragma unroll
-        for (int t = 0; t < DT; ++t) dst[16 * t] = M::round(oacc[t][i] * inv);
+        for (int i = 0; i < 4; ++i) lr[i] = from_lane(lsum, 4 * q + i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int R = row0 + 16 * rb + 4 * q + i;
+            if (R >= rows) continue;
+            const float inv = a.v_scale / lr[i];
+            uint16_t* dst = out + ((int64_t)(first + R / G) * Hq + g * G + R % G) * D + c;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) dst[16 * t] = M::round(oacc[rb][t][i] * inv);
+        }
     }
 }
 
-template <int QT, int KVT, int D>
+template <int QT, int KVT, int D, bool BT_LDS>
 int launch_g(const PrefillArgs& a, int group_size, int64_t grid, hipStream_t st) {
     const dim3 g3((unsigned)grid), block(kThreads);
     switch (group_size) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 1>), g3, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 2>), g3, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 4>), g3, block, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 8>), g3, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 1, BT_LDS>), g3, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 2, BT_LDS>), g3, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 4, BT_LDS>), g3, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 8, BT_LDS>), g3, block, 0, st, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
@@ -341,8 +399,12 @@ int launch_g(const PrefillArgs& a, int group_size, int64_t grid, hipStream_t st)
 
 template <int QT, int KVT>
 int launch_d(const PrefillArgs& a, int head_dim, int group_size, int64_t grid, hipStream_t st) {
-    if (head_dim == 64) return launch_g<QT, KVT, 64>(a, group_size, grid, st);
-    return launch_g<QT, KVT, 128>(a, group_size, grid, st);
+    const bool bt_lds = a.max_blocks_per_seq <= kMaxBt;
+    if (head_dim == 64)
+        return bt_lds ? launch_g<QT, KVT, 64, true>(a, group_size, grid, st)
+                      : launch_g<QT, KVT, 64, false>(a, group_size, grid, st);
+    return bt_lds ? launch_g<QT, KVT, 128, true>(a, group_size, grid, st)
+                  : launch_g<QT, KVT, 128, false>(a, group_size, grid, st);
 }
 
 }  // namespace
