@@ -177,7 +177,8 @@ def upload(b, torch, pa, copies: int):
 
 def cpu_baseline(b, budget_s: float = 20.0) -> dict:
     """The oracle, as it stands, on a bounded sample: whole sequences of the
-    same batch, taken in order until about `budget_s` seconds are spent."""
+    same batch, taken in order (and round again when the batch is done) until
+    about `budget_s` seconds are spent."""
     import oracle
 
     try:
@@ -195,7 +196,8 @@ def cpu_baseline(b, budget_s: float = 20.0) -> dict:
         ctx.__enter__()
     try:
         done, tokens, t_total = [], 0, 0.0
-        order = list(range(b.num_seqs))
+        order = [s for _ in range(1000) for s in range(b.num_seqs)]
+        first = True                         # one untimed call first: one-off set-up is not the oracle's rate
         for s in order:
             if b.kv_dtype == "fp8_e4m3":
                 blocks = sorted(set(b.tables[s]))
@@ -205,12 +207,16 @@ def cpu_baseline(b, budget_s: float = 20.0) -> dict:
                 t0 = time.perf_counter()
                 oracle.paged_decode(b.query[s:s + 1], b.q_dtype, sub, "fp8_e4m3", bt_s, lens[s:s + 1],
                                     b.block_size, b.scale, b.k_scale, b.v_scale)
-                t_total += time.perf_counter() - t0
+                dt = time.perf_counter() - t0
             else:
                 t0 = time.perf_counter()
                 oracle.paged_decode(b.query[s:s + 1], b.q_dtype, pool, b.kv_dtype, bt[s:s + 1], lens[s:s + 1],
                                     b.block_size, b.scale)
-                t_total += time.perf_counter() - t0
+                dt = time.perf_counter() - t0
+            if first:
+                first = False
+                continue
+            t_total += dt
             done.append(s)
             tokens += int(lens[s])
             if t_total >= budget_s:
@@ -224,8 +230,8 @@ def cpu_baseline(b, budget_s: float = 20.0) -> dict:
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{len(done)} of {b.num_seqs} sequences ({tokens} context tokens) of the same batch, "
-                  f"float64 numpy decode, {t_total:.1f} s",
+        "sample": f"{len(done)} sequence decodes ({len(done) / b.num_seqs:.2f} passes over the "
+                  f"{b.num_seqs}-sequence batch, {tokens} context tokens), float64 numpy, {t_total:.1f} s",
         "tokens_per_s_per_layer": round(len(done) / t_total, 3),
     }
 
