@@ -150,3 +150,26 @@ def test_peaked_softmax_precision(qd, kvd):
     ref = oracle.paged_prefill(b.query, qd, want_pool, kvd, b.block_table_array(), b.context_lens,
                                b.cu_seqlens, 16, b.scale, b.k_scale, b.v_scale)
     assert_decode_close(oracle.to_f64(host_bits(out), qd), ref, b)
+
+
+@pytest.mark.parametrize("kvd", ["f16", "fp8_e4m3"])
+def test_wide_block_tables_read_in_place(kvd):
+    """Tables wider than the 2048 entries the kernel stages in LDS take the
+    variant that reads the table in place: same rows, bit for bit, as the
+    staged variant on the same data (narrow tables), and within tolerance of
+    the oracle."""
+    qd = "bf16" if kvd == "fp8_e4m3" else kvd
+    args = ("wide", 74, [260, 33, 129], [100, 33, 64], 16, 4, 128, 16, qd, kvd)
+    narrow = make_prefill(*args)
+    wide = make_prefill(*args, max_blocks_per_seq=2100)
+    assert narrow.tables == wide.tables
+    outs = []
+    for b in (narrow, wide):
+        pool = _start_pool(b)
+        dev, out = _gpu_prompt(b, pool)
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    want_pool = _oracle_pool(wide, _start_pool(wide))
+    ref = oracle.paged_prefill(wide.query, qd, want_pool, kvd, wide.block_table_array(), wide.context_lens,
+                               wide.cu_seqlens, 16, wide.scale, wide.k_scale, wide.v_scale)
+    assert_decode_close(oracle.to_f64(host_bits(outs[1]), qd), ref, wide)
