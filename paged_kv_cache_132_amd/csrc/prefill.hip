@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int k = 0; k < KSTEPS; ++k)
             qop[rb][k] = __builtin_bit_cast(Vec, *reinterpret_cast<const uint4*>(qp + 32 * k));
     }
+    const int pos_first = L - n + row0 / G;              // the wave's earliest query
     const int last_row = min(tile * kRows + kRows, rows) - 1;
     const int p_max = L - n + last_row / G;              // the latest query of the workgroup
     const int n_tiles = p_max / kKeys + 1;
@@ -273,7 +274,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int rb = 0; rb < kRB; ++rb) sacc[rb][u] = M::run(kf, qop[rb][k], sacc[rb][u]);
             }
         }
-        // online softmax (lane: keys 4q+i and 16+4q+i of row c of each block)
+        // online softmax (lane: keys 4q+i and 16+4q+i of row c of each block).
+        // Only tiles that reach past the wave's earliest query need the mask.
+        const bool masked = kt * kKeys + kKeys - 1 > pos_first;
         Vec pop[kRB], pop_lo[kRB];
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) {
@@ -284,7 +287,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = kt * kKeys + 16 * u + 4 * q + i;
-                    const float v = key <= pos[rb] ? sacc[rb][u][i] * a.score_scale : -INFINITY;
+                    float v = sacc[rb][u][i] * a.score_scale;
+                    if (masked) v = key <= pos[rb] ? v : -INFINITY;
                     sc[4 * u + i] = v;
                     mx = fmaxf(mx, v);
                 }
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             float psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pe = sc[e] == -INFINITY ? 0.f : fast_exp2(sc[e] - m_new);
+                const float pe = fast_exp2(sc[e] - m_new);     // masked: 2^-inf = 0
                 const uint16_t pb = M::round(pe);
                 psum += M::widen(pb);
                 pw[e >> 1] |= (uint32_t)pb << (16 * (e & 1));
