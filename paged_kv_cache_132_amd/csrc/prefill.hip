@@ -70,6 +70,16 @@ __device__ __forceinline__ float shfl_xor(float x, int m) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, x)));
 }
 
+// max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48, on the VALU: each
+// v_permlane{16,32}_swap with both operands x leaves, in its two results,
+// x of this lane and of lane l ^ 16 (l ^ 32), in some order
+__device__ __forceinline__ float max_across_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float from_lane(float x, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
@@ -293,8 +303,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     mx = fmaxf(mx, v);
                 }
             }
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
+            mx = max_across_rows(mx);
             const float m_new = fmaxf(m_run[rb], mx);          // finite: key 0 precedes every query
             const float alpha = fast_exp2(m_run[rb] - m_new);
             uint32_t pw[4] = {0u, 0u, 0u, 0u}, plw[4] = {0u, 0u, 0u, 0u};   // packed probabilities
