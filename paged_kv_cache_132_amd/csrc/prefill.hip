@@ -51,6 +51,8 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -105,6 +107,12 @@ struct Mma<PA_F16> {
         return __builtin_bit_cast(uint16_t, (_Float16)x);
     }
     static __device__ __forceinline__ float widen(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+    // two values rounded (RNE) into one packed word, and back
+    static __device__ __forceinline__ uint32_t round2(float x, float y) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+    }
+    static __device__ __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+    static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 };
 
 template <>
@@ -115,6 +123,11 @@ struct Mma<PA_BF16> {
     }
     static __device__ __forceinline__ uint16_t round(float x) { return bf16_rne(x); }
     static __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+    static __device__ __forceinline__ uint32_t round2(float x, float y) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+    }
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 };
 
 // 16 fp8 codes -> 16 bf16 bit patterns (exact), as two 16-byte words.
@@ -306,18 +319,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             mx = max_across_rows(mx);
             const float m_new = fmaxf(m_run[rb], mx);          // finite: key 0 precedes every query
             const float alpha = fast_exp2(m_run[rb] - m_new);
-            uint32_t pw[4] = {0u, 0u, 0u, 0u}, plw[4] = {0u, 0u, 0u, 0u};   // packed probabilities
+            uint32_t pw[4], plw[4];     // packed probabilities (k-slot pairs)
             float psum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = fast_exp2(sc[e] - m_new);     // masked: 2^-inf = 0
-                const uint16_t pb = M::round(pe);
-                psum += M::widen(pb);
-                pw[e >> 1] |= (uint32_t)pb << (16 * (e & 1));
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(sc[2 * e] - m_new);         // masked: 2^-inf = 0
+                const float p1 = fast_exp2(sc[2 * e + 1] - m_new);
+                pw[e] = M::round2(p0, p1);
+                const float r0 = M::lo(pw[e]), r1 = M::hi(pw[e]);
+                psum += r0;
+                psum += r1;
                 if constexpr (SPLIT) {
-                    const uint16_t pl = M::round(pe - M::widen(pb));   // the difference is exact in fp32
-                    psum += M::widen(pl);
-                    plw[e >> 1] |= (uint32_t)pl << (16 * (e & 1));
+                    plw[e] = M::round2(p0 - r0, p1 - r1);              // the differences are exact in fp32
+                    psum += M::lo(plw[e]);
+                    psum += M::hi(plw[e]);
                 }
             }
             l_lane[rb] = l_lane[rb] * alpha + psum;
