@@ -10,17 +10,20 @@ each step reads its pool from HBM rather than from the 256 MB last-level
 cache.
 
 Steps run twice: eagerly, with HIP events around every launch (the per-kernel
-breakdown), and as replays of a HIP graph holding the same three launches
-(the step time a decode loop sees once launch gaps are gone).  Each graph's
-output is checked against the eager output before timing.
+breakdown), and as replays of a HIP graph holding the same launches (the step
+time a decode loop sees once launch gaps are gone).  Each graph's output is
+checked against the eager output before timing.  A labelled warm figure
+(warm_ms_per_step) replays one graph on one pool copy, so caches may hold
+part of the pool.
 
 Prints one JSON line:
   value       KV-read GB/s of the whole step (algorithmic bytes / graph-replayed
               step time; the eager step time is reported beside it)
-  roofline    the attention kernel's (pa_decode_partials) algorithmic bytes /
-              its mean duration from HIP events recorded around every launch
-              in the timed region, against the 8 TB/s HBM peak; the whole
-              pa_decode call (attention + split-K merge) is reported beside it
+  roofline    the attention kernel's algorithmic bytes (the write's included
+              when it is fused) / its mean duration from HIP events recorded
+              around every launch in the timed region, against the 8 TB/s HBM
+              peak; the whole call (attention + split-K merge) is reported
+              beside it
   cpu_baseline  the float64 CPU oracle on the same batch (1 BLAS thread)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama7b]
@@ -470,7 +473,7 @@ def run_decode(args, torch, pa, b) -> dict:
     wall = time.perf_counter() - t0
     eager_ms_step = wall * 1e3 / args.steps
 
-    graph_ms_step = None
+    graph_ms_step = warm_ms_step = None
     if not args.eager:
         # one graph per pool copy, each holding write + attention + merge
         ref = out.clone()
@@ -503,6 +506,13 @@ def run_decode(args, torch, pa, b) -> dict:
             graphs[(args.warmup + i) % copies].replay()
         torch.cuda.synchronize()
         graph_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        # labelled warm figure: every step on the same pool copy, so the L2s
+        # and the MALL may still hold part of it from the step before
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[0].replay()
+        torch.cuda.synchronize()
+        warm_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
         del graphs
 
     write_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
@@ -548,6 +558,7 @@ def run_decode(args, torch, pa, b) -> dict:
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_launch": "hip_graph" if graph_ms_step is not None else "eager",
+        "warm_ms_per_step": round(warm_ms_step, 4) if graph_ms_step is not None else None,
         "step_kernels": ("pa_decode_write_partials (cache write fused), pa_decode_merge" if fused else
                          "pa_cache_write, pa_decode_partials, pa_decode_merge"),
         "eager_ms_per_step": round(eager_ms_step, 4),
