@@ -5,10 +5,13 @@
 // §4.2]: token i of sequence s's run sits at position L_s - n_s + i, so the
 // last block is written only as far as the tokens it holds).
 //
-// One thread moves 8 elements (16 bytes of a 16-bit source row).  Consecutive
-// threads cover consecutive 16-byte pieces of one (row, KV head, K|V) row, so
-// each row is one contiguous, fully coalesced segment on both sides.  A
-// packed row finds its sequence by binary search over cu_seqlens.
+// Workgroup = (source row, K or V, piece of up to 16 KiB of that half-row).
+// The row's slot -- sequence, position, physical block -- is found once per
+// workgroup from wave-uniform values (a packed row by binary search over
+// cu_seqlens).  A half-row (all KV heads of one token) is contiguous both in
+// the source [rows, num_kv_heads, head_dim] and in its pool slot, so thread
+// chunks of 16 source bytes map to the same element offsets on both sides
+// and every workgroup reads and writes one contiguous segment.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -20,20 +23,15 @@ namespace pa {
 namespace {
 
 constexpr int kWriteThreads = 256;
-constexpr int kElemsPerThread = 8;
+constexpr int kElemsPerThread = 8;                   // one 16-byte chunk of a 16-bit source
+constexpr int kChunksPerThread = 4;
+constexpr int kChunksPerGroup = kWriteThreads * kChunksPerThread;
 
 template <int SRC, int KVT>
 __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a) {
-    const int chunks = a.head_dim / kElemsPerThread;
-    const int64_t total = (int64_t)a.num_rows * a.num_kv_heads * 2 * chunks;
-    const int64_t i = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
-    if (i >= total) return;
-    const int c = (int)(i % chunks);
-    int64_t rest = i / chunks;
-    const int kv = (int)(rest & 1);
-    rest >>= 1;
-    const int g = (int)(rest % a.num_kv_heads);
-    const int row = (int)(rest / a.num_kv_heads);
+    const int row = blockIdx.x;
+    const int kv = blockIdx.y & 1;
+    const int piece = blockIdx.y >> 1;
 
     int s, t;
     if (a.cu_seqlens == nullptr) {
@@ -60,37 +58,40 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
     if (blk < 0 || blk >= a.num_blocks) return;
     const int off = t - lb * a.block_size;
 
-    const int64_t src_elem = ((int64_t)row * a.num_kv_heads + g) * a.head_dim + c * kElemsPerThread;
-    const int64_t dst_elem =
-        (((int64_t)blk * 2 + kv) * a.block_size + off) * (int64_t)a.num_kv_heads * a.head_dim +
-        (int64_t)g * a.head_dim + c * kElemsPerThread;
-    const uint4 src = *reinterpret_cast<const uint4*>(
-        static_cast<const uint16_t*>(kv ? a.value : a.key) + src_elem);
-
-    if constexpr (KVT != PA_FP8_E4M3) {
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kv_pool) + dst_elem) = src;
-    } else {
-        const float scale = kv ? a.v_scale : a.k_scale;
-        const uint32_t w[4] = {src.x, src.y, src.z, src.w};
-        uint32_t packed[2] = {0u, 0u};
+    const int64_t half = (int64_t)a.num_kv_heads * a.head_dim;        // elements of one token's K (or V)
+    const int n_chunks = (int)(half / kElemsPerThread);
+    const uint16_t* src = static_cast<const uint16_t*>(kv ? a.value : a.key) + (int64_t)row * half;
+    const int64_t dst_elem = (((int64_t)blk * 2 + kv) * a.block_size + off) * half;
+    const float scale = kv ? a.v_scale : a.k_scale;
 #pragma unroll
-        for (int e = 0; e < kElemsPerThread; ++e) {
-            const uint32_t h = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            const float y = __fdiv_rn(widen<SRC>(h), scale);
-            packed[e >> 2] |= e4m3_from_float(y) << ((e & 3) * 8);
+    for (int u = 0; u < kChunksPerThread; ++u) {
+        const int j = piece * kChunksPerGroup + u * kWriteThreads + threadIdx.x;
+        if (j >= n_chunks) break;
+        const uint4 w = *reinterpret_cast<const uint4*>(src + (int64_t)j * kElemsPerThread);
+        if constexpr (KVT != PA_FP8_E4M3) {
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kv_pool) + dst_elem + (int64_t)j * kElemsPerThread) = w;
+        } else {
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < kElemsPerThread; ++e) {
+                const uint32_t h = (ws[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+                const float y = __fdiv_rn(widen<SRC>(h), scale);
+                packed[e >> 2] |= e4m3_from_float(y) << ((e & 3) * 8);
+            }
+            *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.kv_pool) + dst_elem + (int64_t)j * kElemsPerThread) =
+                make_uint2(packed[0], packed[1]);
         }
-        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.kv_pool) + dst_elem) =
-            make_uint2(packed[0], packed[1]);
     }
 }
 
 template <int SRC, int KVT>
 int launch_typed(const WriteArgs& a, hipStream_t stream) {
-    const int64_t total = (int64_t)a.num_rows * a.num_kv_heads * 2 * (a.head_dim / kElemsPerThread);
-    const int64_t blocks = (total + kWriteThreads - 1) / kWriteThreads;
-    if (blocks == 0) return 0;
-    hipLaunchKernelGGL((cache_write_kernel<SRC, KVT>), dim3((unsigned)blocks), dim3(kWriteThreads),
-                       0, stream, a);
+    if (a.num_rows <= 0) return 0;
+    const int64_t n_chunks = (int64_t)a.num_kv_heads * a.head_dim / kElemsPerThread;
+    const int64_t pieces = (n_chunks + kChunksPerGroup - 1) / kChunksPerGroup;
+    const dim3 grid((unsigned)a.num_rows, (unsigned)(2 * pieces));
+    hipLaunchKernelGGL((cache_write_kernel<SRC, KVT>), grid, dim3(kWriteThreads), 0, stream, a);
     return (int)hipGetLastError();
 }
 
