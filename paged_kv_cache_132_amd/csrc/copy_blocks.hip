@@ -36,10 +36,23 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
     uint8_t* d = a.dst + (int64_t)dst * a.block_bytes;
     const int64_t base = piece * kCopyPiece + (int64_t)threadIdx.x * 16;
     u32x4 v[kCopyUnroll];
+    if ((piece + 1) * kCopyPiece <= a.block_bytes) {
+        // a whole piece (every piece when blocks are multiples of 16 KiB):
+        // all loads in flight together, then all stores
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s + base + u * kCopyThreads * 16));
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(d + base + u * kCopyThreads * 16));
+        return;
+    }
+    // the block's last, partial piece: offsets past the end re-read its last
+    // 16 bytes and store nothing
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
-        const int64_t off = base + (int64_t)u * kCopyThreads * 16;
-        if (off < a.block_bytes) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s + off));
+        const int64_t off = min(base + (int64_t)u * kCopyThreads * 16, a.block_bytes - 16);
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s + off));
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
