@@ -326,8 +326,10 @@ def prefill_flops(b) -> int:
 def bench_prefill(args, torch, pa) -> int:
     """The prompt stage on the packed prompt batch of [CANN notes §1.2]:
     8 fresh prompts of 128..2048 tokens (5256 in all), 32/32 heads,
-    head_dim 128, fp16, block size 16.  One step = pa_cache_write_tokens of
-    all 5256 tokens + pa_prefill."""
+    head_dim 128, fp16, block size 16.  One step = the write of all 5256
+    tokens and the causal attention: pa_prefill_write (one launch that does
+    both) by default, pa_cache_write_tokens + pa_prefill with
+    --separate-write."""
     import oracle
     from workloads import make_prefill_mixed
 
@@ -344,13 +346,19 @@ def bench_prefill(args, torch, pa) -> int:
     mx = int(b.new_lens.max())
     stream = torch.cuda.current_stream()
 
+    fused = not args.separate_write
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        pa.cache_write_tokens(pool, k, v, bt, lens, cu)
+        if not fused:
+            pa.cache_write_tokens(pool, k, v, bt, lens, cu)
         if ev is not None:
             ev[1].record(stream)
-        pa.prefill(q, pool, bt, lens, cu, b.scale, out=out, max_new_tokens=mx)
+        if fused:
+            pa.prefill(q, pool, bt, lens, cu, b.scale, out=out, max_new_tokens=mx, new_key=k, new_value=v)
+        else:
+            pa.prefill(q, pool, bt, lens, cu, b.scale, out=out, max_new_tokens=mx)
         if ev is not None:
             ev[2].record(stream)
 
@@ -367,8 +375,8 @@ def bench_prefill(args, torch, pa) -> int:
     attn = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e3
     attn_us = float(attn.mean())
     achieved = flops / (attn_us * 1e-6) / 1e12
-    log(f"prefill: attention {attn_us:.1f} us ({achieved:.0f} TFLOP/s), write {write_us:.1f} us, "
-        f"step {ms_step * 1e3:.1f} us")
+    log(f"prefill: attention {attn_us:.1f} us ({achieved:.0f} TFLOP/s), "
+        f"{'write fused' if fused else f'write {write_us:.1f} us'}, step {ms_step * 1e3:.1f} us")
     res = {
         "metric": "paged prefill attention TFLOP/s (causal, packed prompts), 1 GPU",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -377,9 +385,10 @@ def bench_prefill(args, torch, pa) -> int:
         "config": {"workload": b.name, "num_seqs": b.num_seqs, "num_tokens": b.num_tokens,
                    "num_heads": b.num_heads, "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
                    "block_size": b.block_size, "seed": b.seed},
+        "step_kernels": "pa_prefill_write (write fused)" if fused else "pa_cache_write_tokens, pa_prefill",
         "prefill_kernel_us": round(attn_us, 2),
         "prefill_kernel_us_p10_p50_p90": [round(float(np.percentile(attn, x)), 2) for x in (10, 50, 90)],
-        "write_tokens_kernel_us": round(write_us, 2),
+        "write_tokens_kernel_us": None if fused else round(write_us, 2),
         "prefill_tokens_per_s_per_layer": round(b.num_tokens / (ms_step * 1e-3), 1),
         "flops": flops,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0, "unit": "TFLOP/s",

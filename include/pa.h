@@ -283,6 +283,32 @@ pa_status pa_prefill(void* out, const void* query, pa_dtype q_dtype, const void*
                      int32_t num_blocks, float scale, float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_prefill_write -- pa_cache_write_tokens and pa_prefill in one call: the
+ * prompt kernel writes the new tokens' K and V as it goes ([CANN notes
+ * §4.2]).  With 16-bit KV this is one launch: each workgroup stores the rows
+ * of the new tokens its own queries belong to, and the attention reads new
+ * tokens from key / value rather than from the pool, so no workgroup waits
+ * for another.  With fp8 KV (the attention must see the encoded codes) it is
+ * the two launches, on the same stream.
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_dim] of src_dtype, rows as
+ *                 in pa_cache_write_tokens; 16-bit KV needs src_dtype ==
+ *                 kv_dtype (else PA_ERR_UNSUPPORTED); 16-byte aligned.
+ *   The other arguments, the results and the errors are those of pa_prefill.
+ *   The 16-bit form writes exactly the rows pa_prefill attends with (a
+ *   sequence with n_s > L_s, or beyond max_new_tokens, is neither written nor
+ *   attended); the pool afterwards is bit for bit what pa_cache_write_tokens
+ *   leaves for every other sequence, and out is bit for bit pa_prefill's.
+ */
+pa_status pa_prefill_write(void* out, const void* query, pa_dtype q_dtype, void* kv_pool, pa_dtype kv_dtype,
+                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens,
+                           int32_t num_seqs, int32_t num_tokens, int32_t max_new_tokens, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t num_blocks, float scale, float k_scale,
+                           float v_scale, void* stream, const void* key, const void* value,
+                           pa_dtype src_dtype);
+
+/*
  * pa_copy_blocks -- copy whole KV blocks from one pool to another of the same
  * block geometry: for each pair i, block block_mapping[2i + 1] of dst_pool
  * becomes a byte copy of block block_mapping[2i] of src_pool (K half and V

@@ -22,8 +22,8 @@ STATUS_NAMES = {
     8: "PA_ERR_POOL_EXHAUSTED", 9: "PA_ERR_UNKNOWN_SEQUENCE",
 }
 EXPORTED = ("pa_cache_write", "pa_cache_write_tokens", "pa_copy_blocks", "pa_decode", "pa_decode_partials",
-            "pa_decode_merge", "pa_decode_write", "pa_decode_write_partials", "pa_decode_workspace_size", "pa_decode_partition_size", "pa_prefill",
-            "pa_status_string",
+            "pa_decode_merge", "pa_decode_write", "pa_decode_write_partials", "pa_decode_workspace_size",
+            "pa_decode_partition_size", "pa_prefill", "pa_prefill_write", "pa_status_string",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
             "pa_bm_free_sequence", "pa_bm_take_copies", "pa_bm_sequence_length", "pa_bm_block_table",
             "pa_bm_ref_count", "pa_bm_stats_get")
@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
         lib.pa_prefill.restype = ctypes.c_int
         lib.pa_prefill.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp,
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, vp]
+        lib.pa_prefill_write.restype = ctypes.c_int
+        lib.pa_prefill_write.argtypes = lib.pa_prefill.argtypes + [vp, vp, ctypes.c_int]
         lib.pa_copy_blocks.restype = ctypes.c_int
         lib.pa_copy_blocks.argtypes = [vp, i32, vp, i32, ctypes.c_int, i32, i32, i32, vp, i32, vp]
         for fn in (lib.pa_decode_write, lib.pa_decode_write_partials):
@@ -192,9 +194,12 @@ def cache_write_tokens(kv_pool: torch.Tensor, key: torch.Tensor, value: torch.Te
 def prefill(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tensor,
             context_lens: torch.Tensor, cu_seqlens: torch.Tensor, scale: float, k_scale: float = 1.0,
             v_scale: float = 1.0, max_new_tokens: int | None = None, out: torch.Tensor | None = None,
-            stream=None) -> torch.Tensor:
+            stream=None, new_key: torch.Tensor | None = None,
+            new_value: torch.Tensor | None = None) -> torch.Tensor:
     """Causal attention of packed new queries [num_tokens, num_heads, head_dim] over
-    their own sequences in the paged pool; returns out of query's shape and dtype."""
+    their own sequences in the paged pool; returns out of query's shape and dtype.
+    new_key / new_value ([num_tokens, num_kv_heads, head_dim]): write the new
+    tokens in the same call (pa_prefill_write), as pa_cache_write_tokens would."""
     nb, bs, hkv, d = _pool_dims(kv_pool)
     if query.dim() != 3 or query.shape[2] != d or not query.is_contiguous():
         raise ValueError("query must be a contiguous [num_tokens, num_heads, head_dim] tensor")
@@ -206,11 +211,18 @@ def prefill(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tens
         out = torch.empty_like(query)
     elif out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
         raise ValueError("out must match query")
-    st = load().pa_prefill(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), pa_dtype(kv_pool),
-                           _ptr(block_tables), _ptr(context_lens), _ptr(cu_seqlens), B, T,
-                           _max_new(cu_seqlens, max_new_tokens), hq, hkv, d, bs, mb, nb, float(scale),
-                           float(k_scale), float(v_scale), _stream(stream))
-    _check(st, "pa_prefill")
+    args = (_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), pa_dtype(kv_pool),
+            _ptr(block_tables), _ptr(context_lens), _ptr(cu_seqlens), B, T,
+            _max_new(cu_seqlens, max_new_tokens), hq, hkv, d, bs, mb, nb, float(scale),
+            float(k_scale), float(v_scale), _stream(stream))
+    if new_key is None:
+        st = load().pa_prefill(*args)
+    else:
+        if new_value is None or new_key.shape != (T, hkv, d) or new_value.shape != new_key.shape \
+                or not (new_key.is_contiguous() and new_value.is_contiguous()) or new_value.dtype != new_key.dtype:
+            raise ValueError("new_key/new_value must be contiguous [num_tokens, num_kv_heads, head_dim] of one dtype")
+        st = load().pa_prefill_write(*args, _ptr(new_key), _ptr(new_value), pa_dtype(new_key))
+    _check(st, "pa_prefill_write" if new_key is not None else "pa_prefill")
     return out
 
 

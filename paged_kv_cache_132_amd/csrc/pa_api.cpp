@@ -227,11 +227,13 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
     return p.bytes;
 }
 
-pa_status pa_prefill(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool, pa_dtype kv_dtype,
-                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens,
-                     int32_t num_seqs, int32_t num_tokens, int32_t max_new_tokens, int32_t num_heads,
-                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                     int32_t num_blocks, float scale, float k_scale, float v_scale, void* stream) {
+static pa_status prefill_impl(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
+                              pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_tokens,
+                              int32_t max_new_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                              float k_scale, float v_scale, void* stream, const void* new_key,
+                              const void* new_value) {
     // the per-call checks are those of pa_decode, with no split-K partition
     pa_status st = check_decode_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens,
                                      num_seqs, num_heads, num_kv_heads, head_dim, block_size,
@@ -262,7 +264,48 @@ pa_status pa_prefill(void* out, const void* query, pa_dtype q_dtype, const void*
     a.num_blocks = num_blocks;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;
+    a.new_key = new_key;
+    a.new_value = new_value;
     return launch_prefill(a, kv_dtype, head_dim, group, max_new_tokens, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_prefill(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool, pa_dtype kv_dtype,
+                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens,
+                     int32_t num_seqs, int32_t num_tokens, int32_t max_new_tokens, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int32_t num_blocks, float scale, float k_scale, float v_scale, void* stream) {
+    return prefill_impl(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens, cu_seqlens, num_seqs,
+                        num_tokens, max_new_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, stream, nullptr, nullptr);
+}
+
+pa_status pa_prefill_write(void* out, const void* query, pa_dtype q_dtype, void* kv_pool, pa_dtype kv_dtype,
+                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens,
+                           int32_t num_seqs, int32_t num_tokens, int32_t max_new_tokens, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t num_blocks, float scale, float k_scale,
+                           float v_scale, void* stream, const void* key, const void* value,
+                           pa_dtype src_dtype) {
+    if (kv_dtype == PA_FP8_E4M3) {
+        // the attention reads the encoded codes: write first, then attend
+        pa_status st = pa_cache_write_tokens(kv_pool, kv_dtype, key, value, src_dtype, block_tables,
+                                             context_lens, cu_seqlens, num_seqs, num_tokens, num_kv_heads,
+                                             head_dim, block_size, max_blocks_per_seq, num_blocks, k_scale,
+                                             v_scale, stream);
+        if (st != PA_OK) return st;
+        return pa_prefill(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens, cu_seqlens,
+                          num_seqs, num_tokens, max_new_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, stream);
+    }
+    if (!known_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
+    if (src_dtype != kv_dtype) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > 0 && num_tokens > 0 && max_new_tokens > 0) {
+        if (!key || !value) return PA_ERR_NULL_POINTER;
+        if (!aligned16(key) || !aligned16(value)) return PA_ERR_MISALIGNED;
+    }
+    return prefill_impl(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens, cu_seqlens, num_seqs,
+                        num_tokens, max_new_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, stream, key, value);
 }
 
 // Device address of a pool: device memory of the current device, or host

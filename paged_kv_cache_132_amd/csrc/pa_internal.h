@@ -100,6 +100,11 @@ struct PrefillArgs {
     int32_t block_size, block_shift, max_blocks_per_seq, num_blocks;
     float score_scale;          // scale * k_scale * log2(e)
     float v_scale;
+    // Fused prompt-stage write (null: none): the new tokens' K/V rows
+    // [num_tokens, num_kv_heads, head_dim] in the (16-bit) pool dtype, stored
+    // into their slots and read from here by the attention.
+    const void* new_key;
+    const void* new_value;
 };
 
 struct CopyArgs {

@@ -145,7 +145,7 @@ __device__ __forceinline__ void widen16_fp8(uint4 w, uint4& lo, uint4& hi) {
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-template <int QT, int KVT, int D, int G, bool BT_LDS>
+template <int QT, int KVT, int D, int G, bool BT_LDS, bool WRITE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
     using M = Mma<QT>;
     using Vec = typename M::Vec;
@@ -160,6 +160,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int KSTEPS = D / 32;
     constexpr int DT = D / 16;
     constexpr bool SPLIT = QT == PA_BF16 && KVT == PA_BF16;   // P = bf16 part + bf16 remainder
+    static_assert(!WRITE || KVT != PA_FP8_E4M3, "the fused write moves 16-bit rows unchanged");
 
     __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeys * KS];
     __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kKeys * VS];
@@ -214,6 +215,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int i = tid; i < nblk; i += kThreads) s_bt[i] = bt_row[i];
         __syncthreads();
     }
+    auto block_of = [&](int t) {
+        int blk;
+        if constexpr (BT_LDS) blk = s_bt[t >> shift];
+        else blk = bt_row[t >> shift];
+        return blk;
+    };
+
+    // ---- fused prompt-stage write ([CANN notes §4.2]: the prompt kernel
+    // writes K and V as it goes).  This workgroup stores the K and V rows of
+    // head g for the new tokens its own query rows belong to; every
+    // workgroup reads new tokens' K and V from the source rows instead of the
+    // pool, so no workgroup waits for another's stores.
+    if constexpr (WRITE) {
+        constexpr int CPR = D / 8;                          // 16-byte chunks per head row
+        const int i0 = tile * kRows / G;
+        const int i1 = min(n, (tile + 1) * kRows / G);
+        const int total = (i1 - i0) * 2 * CPR;
+        const int64_t row_elems = (int64_t)Hkv * D;
+        uint16_t* pool16 = static_cast<uint16_t*>(const_cast<void*>(a.kv_pool));
+        // chunk x: 16 bytes of the K (or V) row of new token i0 + x / (2 CPR),
+        // head g; past `total` the source is re-read and nothing is stored
+        struct Job {
+            const uint4* src;
+            uint4* dst;
+        };
+        auto job = [&](int x) {
+            const int xc = min(x, total - 1);
+            const int c = xc % CPR;
+            const int kvh = (xc / CPR) & 1;
+            const int i = i0 + xc / (2 * CPR);
+            const int t = L - n + i;
+            const int blk = block_of(t);
+            Job j;
+            j.src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kvh ? a.new_value : a.new_key) +
+                                                   ((int64_t)(first + i) * Hkv + g) * D + c * 8);
+            const int64_t drow = ((int64_t)blk * 2 + kvh << shift) + (t & (a.block_size - 1));
+            j.dst = (x < total && blk >= 0 && blk < a.num_blocks)
+                        ? reinterpret_cast<uint4*>(pool16 + drow * row_elems + g * D + c * 8) : nullptr;
+            return j;
+        };
+        for (int x0 = tid; x0 < total; x0 += 4 * kThreads) {   // four chunks in flight per thread
+            const Job j0 = job(x0), j1 = job(x0 + kThreads), j2 = job(x0 + 2 * kThreads), j3 = job(x0 + 3 * kThreads);
+            const uint4 w0 = *j0.src, w1 = *j1.src, w2 = *j2.src, w3 = *j3.src;
+            if (j0.dst) *j0.dst = w0;
+            if (j1.dst) *j1.dst = w1;
+            if (j2.dst) *j2.dst = w2;
+            if (j3.dst) *j3.dst = w3;
+        }
+    }
 
     // ---- K/V tile loads ---------------------------------------------------------
     const int64_t row_bytes = (int64_t)Hkv * D * KB;
@@ -231,9 +281,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int key = ci / CPK;
         const int ch = ci % CPK;
         const int t = min(kt * kKeys + key, L - 1);   // keys past the last position are masked
-        int blk;
-        if constexpr (BT_LDS) blk = s_bt[t >> shift];
-        else blk = bt_row[t >> shift];
+        if (WRITE && t >= L - n) {                    // a new token: its source row
+            const int64_t src = ((int64_t)(first + t - (L - n)) * Hkv + g) * D + ch * EPC;
+            kd = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.new_key) + src);
+            vd = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.new_value) + src);
+            return;
+        }
+        int blk = block_of(t);
         blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
         const int64_t krow = ((int64_t)blk * 2 << shift) + (t & (a.block_size - 1));
         const uint8_t* kp = pool + krow * row_bytes + (int64_t)(g * D + ch * EPC) * KB;
@@ -412,27 +466,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 }
 
-template <int QT, int KVT, int D, bool BT_LDS>
+template <int QT, int KVT, int D, bool BT_LDS, bool WRITE>
 int launch_g(const PrefillArgs& a, int group_size, int64_t grid, hipStream_t st) {
     const dim3 g3((unsigned)grid), block(kThreads);
     switch (group_size) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 1, BT_LDS>), g3, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 2, BT_LDS>), g3, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 4, BT_LDS>), g3, block, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 8, BT_LDS>), g3, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 1, BT_LDS, WRITE>), g3, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 2, BT_LDS, WRITE>), g3, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 4, BT_LDS, WRITE>), g3, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<QT, KVT, D, 8, BT_LDS, WRITE>), g3, block, 0, st, a); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }
 
-template <int QT, int KVT>
+template <int QT, int KVT, bool WRITE>
 int launch_d(const PrefillArgs& a, int head_dim, int group_size, int64_t grid, hipStream_t st) {
     const bool bt_lds = a.max_blocks_per_seq <= kMaxBt;
     if (head_dim == 64)
-        return bt_lds ? launch_g<QT, KVT, 64, true>(a, group_size, grid, st)
-                      : launch_g<QT, KVT, 64, false>(a, group_size, grid, st);
-    return bt_lds ? launch_g<QT, KVT, 128, true>(a, group_size, grid, st)
-                  : launch_g<QT, KVT, 128, false>(a, group_size, grid, st);
+        return bt_lds ? launch_g<QT, KVT, 64, true, WRITE>(a, group_size, grid, st)
+                      : launch_g<QT, KVT, 64, false, WRITE>(a, group_size, grid, st);
+    return bt_lds ? launch_g<QT, KVT, 128, true, WRITE>(a, group_size, grid, st)
+                  : launch_g<QT, KVT, 128, false, WRITE>(a, group_size, grid, st);
 }
 
 }  // namespace
@@ -447,9 +501,15 @@ int launch_prefill(const PrefillArgs& a, pa_dtype kv_dtype, int head_dim, int gr
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t grid = prefill_grid(a.num_seqs, a.num_kv_heads, group_size, max_new_tokens);
     if (grid == 0) return 0;
-    if (kv_dtype == PA_F16) return launch_d<PA_F16, PA_F16>(a, head_dim, group_size, grid, st);
-    if (kv_dtype == PA_BF16) return launch_d<PA_BF16, PA_BF16>(a, head_dim, group_size, grid, st);
-    return launch_d<PA_BF16, PA_FP8_E4M3>(a, head_dim, group_size, grid, st);
+    const bool w = a.new_key != nullptr;                 // fused write: 16-bit KV only
+    if (kv_dtype == PA_F16)
+        return w ? launch_d<PA_F16, PA_F16, true>(a, head_dim, group_size, grid, st)
+                 : launch_d<PA_F16, PA_F16, false>(a, head_dim, group_size, grid, st);
+    if (kv_dtype == PA_BF16)
+        return w ? launch_d<PA_BF16, PA_BF16, true>(a, head_dim, group_size, grid, st)
+                 : launch_d<PA_BF16, PA_BF16, false>(a, head_dim, group_size, grid, st);
+    if (w) return (int)hipErrorInvalidValue;
+    return launch_d<PA_BF16, PA_FP8_E4M3, false>(a, head_dim, group_size, grid, st);
 }
 
 }  // namespace pa

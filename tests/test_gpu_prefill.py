@@ -173,3 +173,37 @@ def test_wide_block_tables_read_in_place(kvd):
     ref = oracle.paged_prefill(wide.query, qd, want_pool, kvd, wide.block_table_array(), wide.context_lens,
                                wide.cu_seqlens, 16, wide.scale, wide.k_scale, wide.v_scale)
     assert_decode_close(oracle.to_f64(host_bits(outs[1]), qd), ref, wide)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_prefill_write_equals_separate_calls(name):
+    """pa_prefill_write (the write inside the prompt kernel for 16-bit KV, the
+    two launches for fp8) leaves the pool bit for bit as pa_cache_write_tokens
+    does and gives pa_prefill's output bit for bit."""
+    lens, new, hq, hkv, d, bs, qd, kvd = CASES[name]
+    b = make_prefill(name, 60 + sorted(CASES).index(name), lens, new, hq, hkv, d, bs, qd, kvd)
+    pool = _start_pool(b)
+    dev_sep, out_sep = _gpu_prompt(b, pool)
+    bt, lens_d, cu = dev_i32(b.block_table_array()), dev_i32(b.context_lens), dev_i32(b.cu_seqlens)
+    dev = dev_pool(pool, kvd)
+    out = pa.prefill(dev16(b.query, qd), dev, bt, lens_d, cu, b.scale, b.k_scale, b.v_scale,
+                     max_new_tokens=int(b.new_lens.max(initial=0)),
+                     new_key=dev16(b.new_key, b.src_dtype), new_value=dev16(b.new_value, b.src_dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dev), host_bits(dev_sep))
+    assert np.array_equal(host_bits(out), host_bits(out_sep))
+
+
+def test_prefill_write_packed_mixed_prompts_full_size():
+    """The 5256-token packed prompt batch through pa_prefill_write: pool and
+    output bit for bit those of the two separate launches."""
+    b = make_prefill_mixed()
+    pool = _start_pool(b)
+    dev_sep, out_sep = _gpu_prompt(b, pool)
+    bt, lens_d, cu = dev_i32(b.block_table_array()), dev_i32(b.context_lens), dev_i32(b.cu_seqlens)
+    dev = dev_pool(pool, "f16")
+    out = pa.prefill(dev16(b.query, "f16"), dev, bt, lens_d, cu, b.scale, max_new_tokens=int(b.new_lens.max()),
+                     new_key=dev16(b.new_key, "f16"), new_value=dev16(b.new_value, "f16"))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dev), host_bits(dev_sep))
+    assert np.array_equal(host_bits(out), host_bits(out_sep))
