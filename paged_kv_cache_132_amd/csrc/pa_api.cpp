@@ -227,13 +227,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
     return p.bytes;
 }
 
-static pa_status prefill_impl(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
-                              pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
-                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_tokens,
-                              int32_t max_new_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
-                              float k_scale, float v_scale, void* stream, const void* new_key,
-                              const void* new_value) {
+// Argument checks of pa_prefill; *work is set when there is anything to launch.
+static pa_status check_prefill_args(const void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
+                                    pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
+                                    const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_tokens,
+                                    int32_t max_new_tokens, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                    int32_t num_blocks, float scale, float k_scale, float v_scale, bool* work) {
+    *work = false;
     // the per-call checks are those of pa_decode, with no split-K partition
     pa_status st = check_decode_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens,
                                      num_seqs, num_heads, num_kv_heads, head_dim, block_size,
@@ -246,6 +247,24 @@ static pa_status prefill_impl(void* out, const void* query, pa_dtype q_dtype, co
     if (num_seqs == 0 || num_tokens == 0 || max_new_tokens == 0) return PA_OK;
     if (!cu_seqlens) return PA_ERR_NULL_POINTER;
     if (!aligned16(cu_seqlens)) return PA_ERR_MISALIGNED;
+    *work = true;
+    return PA_OK;
+}
+
+static pa_status prefill_impl(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
+                              pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t num_tokens,
+                              int32_t max_new_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                              float k_scale, float v_scale, void* stream, const void* new_key,
+                              const void* new_value) {
+    bool work = false;
+    const pa_status st = check_prefill_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens,
+                                            cu_seqlens, num_seqs, num_tokens, max_new_tokens, num_heads,
+                                            num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                            scale, k_scale, v_scale, &work);
+    if (st != PA_OK || !work) return st;
+    const int group = num_heads / num_kv_heads;
     const bool fp8 = kv_dtype == PA_FP8_E4M3;
     PrefillArgs a;
     a.out = out;
@@ -286,12 +305,23 @@ pa_status pa_prefill_write(void* out, const void* query, pa_dtype q_dtype, void*
                            int32_t max_blocks_per_seq, int32_t num_blocks, float scale, float k_scale,
                            float v_scale, void* stream, const void* key, const void* value,
                            pa_dtype src_dtype) {
+    bool work = false;
+    pa_status st = check_prefill_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens,
+                                      cu_seqlens, num_seqs, num_tokens, max_new_tokens, num_heads, num_kv_heads,
+                                      head_dim, block_size, max_blocks_per_seq, num_blocks, scale, k_scale,
+                                      v_scale, &work);
+    if (st != PA_OK) return st;
     if (kv_dtype == PA_FP8_E4M3) {
         // the attention reads the encoded codes: write first, then attend
-        pa_status st = pa_cache_write_tokens(kv_pool, kv_dtype, key, value, src_dtype, block_tables,
-                                             context_lens, cu_seqlens, num_seqs, num_tokens, num_kv_heads,
-                                             head_dim, block_size, max_blocks_per_seq, num_blocks, k_scale,
-                                             v_scale, stream);
+        // (both calls' checks pass before anything is launched)
+        if (src_dtype != PA_BF16 && src_dtype != PA_F16) return known_dtype(src_dtype) ? PA_ERR_UNSUPPORTED
+                                                                                       : PA_ERR_BAD_DTYPE;
+        if (!work) return PA_OK;
+        if (!key || !value) return PA_ERR_NULL_POINTER;
+        if (!aligned16(key) || !aligned16(value)) return PA_ERR_MISALIGNED;
+        st = pa_cache_write_tokens(kv_pool, kv_dtype, key, value, src_dtype, block_tables, context_lens,
+                                   cu_seqlens, num_seqs, num_tokens, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, num_blocks, k_scale, v_scale, stream);
         if (st != PA_OK) return st;
         return pa_prefill(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens, cu_seqlens,
                           num_seqs, num_tokens, max_new_tokens, num_heads, num_kv_heads, head_dim, block_size,
@@ -299,10 +329,9 @@ pa_status pa_prefill_write(void* out, const void* query, pa_dtype q_dtype, void*
     }
     if (!known_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
     if (src_dtype != kv_dtype) return PA_ERR_UNSUPPORTED;
-    if (num_seqs > 0 && num_tokens > 0 && max_new_tokens > 0) {
-        if (!key || !value) return PA_ERR_NULL_POINTER;
-        if (!aligned16(key) || !aligned16(value)) return PA_ERR_MISALIGNED;
-    }
+    if (!work) return PA_OK;
+    if (!key || !value) return PA_ERR_NULL_POINTER;
+    if (!aligned16(key) || !aligned16(value)) return PA_ERR_MISALIGNED;
     return prefill_impl(out, query, q_dtype, kv_pool, kv_dtype, block_tables, context_lens, cu_seqlens, num_seqs,
                         num_tokens, max_new_tokens, num_heads, num_kv_heads, head_dim, block_size,
                         max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, stream, key, value);

@@ -250,3 +250,43 @@ def test_prefill_rejects_bad_arguments(lib, kw, status):
 def test_prefill_without_tokens_is_a_noop(lib):
     assert call_prefill(lib, num_tokens=0, cu_seqlens=None) == 0
     assert call_prefill(lib, max_new_tokens=0, cu_seqlens=None) == 0
+
+
+def call_prefill_write(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, q_dtype=F16, kv_pool=FAKE, kv_dtype=F16, block_tables=FAKE,
+             context_lens=FAKE, cu_seqlens=FAKE, num_seqs=4, num_tokens=40, max_new_tokens=20,
+             num_heads=8, num_kv_heads=8, head_dim=64, block_size=16, max_blocks_per_seq=3, num_blocks=64,
+             scale=0.125, k_scale=1.0, v_scale=1.0, stream=None, key=FAKE, value=FAKE, src_dtype=F16)
+    a.update(kw)
+    return lib.pa_prefill_write(a["out"], a["query"], a["q_dtype"], a["kv_pool"], a["kv_dtype"],
+                                a["block_tables"], a["context_lens"], a["cu_seqlens"], a["num_seqs"],
+                                a["num_tokens"], a["max_new_tokens"], a["num_heads"], a["num_kv_heads"],
+                                a["head_dim"], a["block_size"], a["max_blocks_per_seq"], a["num_blocks"],
+                                a["scale"], a["k_scale"], a["v_scale"], a["stream"], a["key"], a["value"],
+                                a["src_dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=None), NULLP),
+    (dict(value=None), NULLP),
+    (dict(key=FAKE + 4), MISAL),
+    (dict(src_dtype=BF16), UNSUP),
+    (dict(src_dtype=7), DTYPE),
+    (dict(cu_seqlens=None), NULLP),
+    (dict(out=None), NULLP),
+    (dict(head_dim=96), UNSUP),
+    # fp8 KV: the write and the attention are checked before either is launched
+    (dict(q_dtype=BF16, kv_dtype=FP8, src_dtype=FP8), UNSUP),
+    (dict(q_dtype=BF16, kv_dtype=FP8, src_dtype=BF16, key=None), NULLP),
+    (dict(q_dtype=BF16, kv_dtype=FP8, src_dtype=BF16, k_scale=0.0), SHAPE),
+    (dict(q_dtype=F16, kv_dtype=FP8, src_dtype=BF16), UNSUP),
+])
+def test_prefill_write_rejects_bad_arguments(lib, kw, status):
+    assert call_prefill_write(lib, **kw) == status
+
+
+def test_prefill_write_without_tokens_is_a_noop(lib):
+    assert call_prefill_write(lib, num_tokens=0, cu_seqlens=None, key=None, value=None) == 0
+    assert call_prefill_write(lib, max_new_tokens=0, cu_seqlens=None, key=None, value=None) == 0
+    assert call_prefill_write(lib, num_tokens=0, cu_seqlens=None, key=None, value=None, q_dtype=BF16,
+                              kv_dtype=FP8, src_dtype=BF16) == 0
