@@ -11,8 +11,9 @@ import torch
 
 import oracle
 import paged_kv_cache_132_amd as pa
-from tests._gpu import assert_decode_close, dev16, dev_i32, dev_pool, host_bits, poison_unused, pool_of
-from workloads import make_custom
+from tests._gpu import (assert_decode_close, dev16, dev_i32, dev_pool, gpu_fp8_pool_from_source, host_bits,
+                        oracle_decode_sampled, poison_unused, pool_of)
+from workloads import make_custom, make_gqa_fp8, make_llama7b
 
 pytestmark = pytest.mark.gpu
 
@@ -105,3 +106,75 @@ def test_fused_write_two_phase_and_graph():
         torch.cuda.synchronize()
         assert torch.equal(one.view(torch.int16), two.view(torch.int16))
     assert torch.equal(pool_a, pool_b)
+
+
+def _bench_step(b, pool_dev):
+    """The bench's decode step as bench.py times it: tables padded with 0,
+    the planned partition, pa_decode_write_partials then pa_decode_merge."""
+    bt, lens = dev_i32(b.block_table_array(pad=0)), dev_i32(b.context_lens.astype(np.int32))
+    q = dev16(b.query, b.q_dtype)
+    k, v = dev16(b.new_key[0], b.src_dtype), dev16(b.new_value[0], b.src_dtype)
+    ws = torch.zeros(pa.decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.block_size,
+                                              b.max_blocks_per_seq, pa.pa_dtype(pool_dev), 0),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    args = (q, pool_dev, bt, lens, b.scale, b.k_scale, b.v_scale)
+    pa.decode(*args, out=out, workspace=ws, phase="partials", new_key=k, new_value=v)
+    pa.decode(*args, out=out, workspace=ws, phase="merge")
+    torch.cuda.synchronize()
+    return out
+
+
+def _pool_after_write(b, base_blocks):
+    """Oracle pool rows for `blocks` after the step's write: the generated
+    values (fp8: oracle-encoded), then each sequence's newest token written
+    by the oracle's cache write wherever its slot falls in these blocks."""
+    src = "bf16" if b.kv_dtype == "fp8_e4m3" else b.kv_dtype
+
+    def rows(blocks):
+        blocks = [int(x) for x in blocks]
+        if b.kv_dtype == "fp8_e4m3":
+            sub = oracle.encode_pool(b.kv_source[blocks], "bf16", "fp8_e4m3", b.k_scale, b.v_scale)
+        else:
+            sub = b.kv_pool[blocks].copy()
+        pos = {blk: i for i, blk in enumerate(blocks)}
+        for s, (tab, L) in enumerate(zip(b.tables, b.context_lens)):
+            t = int(L) - 1
+            blk = int(tab[t // b.block_size])
+            if blk in pos:
+                sub = oracle.cache_write(sub, b.kv_dtype, b.new_key[0][s:s + 1], b.new_value[0][s:s + 1], src,
+                                         np.array([[pos[blk]]], dtype=np.int32),
+                                         np.array([t % b.block_size + 1], dtype=np.int32), b.block_size,
+                                         b.k_scale, b.v_scale)
+        return sub
+
+    return rows
+
+
+def _check_bench_step(b, pool_dev, seqs):
+    out = _bench_step(b, pool_dev)
+    after = _pool_after_write(b, None)
+    written = sorted({int(tab[(int(L) - 1) // b.block_size]) for tab, L in zip(b.tables, b.context_lens)})
+    rng = np.random.default_rng(31)
+    blocks = sorted(set(written[:64]) | set(rng.choice(b.num_blocks, size=32, replace=False).tolist()))
+    got_blocks = host_bits(pool_dev[torch.tensor(blocks, device="cuda")])
+    assert np.array_equal(got_blocks, after(blocks))
+    ref = oracle_decode_sampled(b, after, b.query, b.block_table_array(), b.context_lens, seqs)
+    assert_decode_close(oracle.to_f64(host_bits(out), b.q_dtype), ref, b, seqs=seqs)
+
+
+def test_llama7b_full_size_bench_step():
+    """The 7B batch at full size through the bench's own step: the written
+    slots bit-exact, sampled outputs within tolerance of the oracle."""
+    b = make_llama7b()
+    lens = b.context_lens
+    _check_bench_step(b, dev_pool(b.kv_pool, "f16"), [int(np.argmin(lens)), int(np.argmax(lens)), 0, 13, 31])
+
+
+def test_gqa_fp8_full_size_bench_step():
+    """GQA-4 over fp8 KV at full size through the bench's own step (matrix-
+    core kernel, write fused): written slots bit-exact, sampled outputs within
+    2e-2 of the oracle."""
+    b = make_gqa_fp8()
+    lens = b.context_lens
+    _check_bench_step(b, gpu_fp8_pool_from_source(b), [int(np.argmin(lens)), int(np.argmax(lens)), 0, 128, 255])
