@@ -36,6 +36,10 @@
 // Two launches instead of a last-arriving-workgroup merge: publishing
 // partials between workgroups inside one kernel needs device-scope fences,
 // and on this part each one writes back and invalidates the XCD's L2.
+//
+// With WRITE (pa_decode_write) the wave that will load a sequence's newest
+// token first stores that token's encoded K/V rows, each lane the bytes it
+// later reads back itself (see the block before the main loop).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>

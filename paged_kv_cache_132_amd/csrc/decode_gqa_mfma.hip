@@ -34,7 +34,9 @@
 //        gets the 8 k-slot tokens of one head_dim column, widened to bf16.
 //        8 MFMAs (16 head_dim columns each) accumulate O[head][d] in fp32.
 //
-// Output, partials and the merge are shared with the vector kernel.
+// Output, partials and the merge are shared with the vector kernel.  With
+// WRITE (pa_decode_write) the 8 lanes whose loads will cover a sequence's
+// newest token store its encoded K/V row first, in the segment that holds it.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
