@@ -64,6 +64,7 @@ constexpr int kRB = 2;                  // 16-row MFMA blocks per wave
 constexpr int kRows = 4 * 16 * kRB;     // (token, head) rows per workgroup
 constexpr int kKeys = 32;               // keys per tile
 constexpr int kMaxBt = 2048;            // block-table entries staged in LDS (longer tables are read in place)
+constexpr float kSlack = 8.f;           // a row's weights stay below 2^8 between rescales
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -371,8 +372,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             }
             mx = max_across_rows(mx);
-            const float m_new = fmaxf(m_run[rb], mx);          // finite: key 0 precedes every query
-            const float alpha = fast_exp2(m_run[rb] - m_new);
+            // The reference max moves only when a row's max grows by more
+            // than kSlack (log2 units): the weights stay below 2^kSlack and
+            // most tiles need no rescale of o at all.
+            const bool grow = mx > m_run[rb] + kSlack;         // always on the first tile (m_run = -inf)
+            const float m_new = grow ? mx : m_run[rb];         // finite: key 0 precedes every query
+            const float alpha = grow ? fast_exp2(m_run[rb] - m_new) : 1.f;
             uint32_t pw[4], plw[4];     // packed probabilities (k-slot pairs)
             float psum = 0.f;
 #pragma unroll
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
             l_lane[rb] = l_lane[rb] * alpha + psum;
             m_run[rb] = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+            if (__builtin_amdgcn_ballot_w64(grow)) {
                 float ar[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ar[i] = from_lane(alpha, 4 * q + i);
