@@ -58,6 +58,7 @@ constexpr int kD = 128;                  // head_dim
 constexpr int kRowStride = 144;          // LDS bytes per staged V row (128 + 16 against bank conflicts)
 constexpr int kStepTokens = 32;
 constexpr int kGqaStages = 2;            // 32-token steps of K/V loads each wave keeps in flight
+constexpr float kSlack = 8.f;            // a head's weights stay below 2^8 between rescales
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -269,9 +270,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
             }
             mx = fmaxf(mx, shfl_xor(mx, 16));
             mx = fmaxf(mx, shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            // a half whose blocks are all dropped can leave m_new at -inf for this step
-            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+            // The reference max moves only when a head's max grows by more
+            // than kSlack (log2 units): weights stay below 2^kSlack and most
+            // steps skip the rescale of O (an AGPR round trip).  A step whose
+            // halves are all dropped leaves mx, and maybe m_run, at -inf.
+            const bool grow = mx > m_run + kSlack;
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
             // probabilities rounded to bf16 once: the same values feed the PV
             // product and the running sum, so the weights normalise exactly
             uint16_t pb[8];
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
             l_lane = l_lane * alpha + psum;
             m_run = m_new;
             // rescale O rows (head 4q+i in register i) when some real head's max moved
-            if (__builtin_amdgcn_ballot_w64(n < G && alpha != 1.f)) {
+            if (__builtin_amdgcn_ballot_w64(n < G && grow)) {
                 float ar[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ar[i] = from_lane(alpha, 4 * q + i);
