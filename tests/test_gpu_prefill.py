@@ -55,6 +55,8 @@ CASES = {
     "empty_runs": ([50, 10, 7], [0, 10, 0], 4, 4, 128, 16, "f16", "f16"),
     "prefix_bs8_f16": ([70, 20, 9], [30, 20, 1], 8, 8, 128, 8, "f16", "f16"),
     "gqa4_fp8_bs8": ([100, 8], [60, 8], 16, 4, 64, 8, "bf16", "fp8_e4m3"),
+    "prefix_gqa8_bf16": ([150, 40, 300], [33, 40, 129], 16, 2, 128, 16, "bf16", "bf16"),
+    "gqa4_f16_d64_bs32": ([70, 200], [70, 65], 16, 4, 64, 32, "f16", "f16"),
 }
 
 
