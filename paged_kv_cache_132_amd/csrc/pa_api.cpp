@@ -242,6 +242,9 @@ static pa_status check_prefill_args(const void* out, const void* query, pa_dtype
     if (st != PA_OK) return st;
     if (num_tokens < 0 || max_new_tokens < 0) return PA_ERR_BAD_SHAPE;
     if ((int64_t)num_tokens * num_heads * head_dim > (int64_t)INT32_MAX * 8) return PA_ERR_BAD_SHAPE;
+    // the prompt kernel addresses within a block in 32 bits
+    if ((int64_t)2 * block_size * num_kv_heads * head_dim * elem_bytes(kv_dtype) > (int64_t)UINT32_MAX)
+        return PA_ERR_BAD_SHAPE;
     const int group = num_heads / num_kv_heads;
     if (prefill_grid(num_seqs, num_kv_heads, group, max_new_tokens) > (int64_t)INT32_MAX) return PA_ERR_BAD_SHAPE;
     if (num_seqs == 0 || num_tokens == 0 || max_new_tokens == 0) return PA_OK;

@@ -66,12 +66,12 @@ constexpr int kKeys = 32;               // keys per tile
 constexpr int kMaxBt = 2048;            // block-table entries staged in LDS (longer tables are read in place)
 constexpr float kSlack = 8.f;           // a row's weights stay below 2^8 between rescales
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+template <bool B>
+struct MaskTag {   // selects the per-tile code with or without the causal mask
+    static constexpr bool value = B;
+};
 
-__device__ __forceinline__ float shfl_xor(float x, int m) {
-    const int lane = __lane_id();
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, x)));
-}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48, on the VALU: each
 // v_permlane{16,32}_swap with both operands x leaves, in its two results,
@@ -101,6 +101,7 @@ struct Mma;
 template <>
 struct Mma<PA_F16> {
     typedef f16x8 Vec;
+    static constexpr uint32_t kOne2 = 0x3C003C00u;   // two 1.0 values
     static __device__ __forceinline__ f32x4 run(Vec a, Vec b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
@@ -119,6 +120,7 @@ struct Mma<PA_F16> {
 template <>
 struct Mma<PA_BF16> {
     typedef bf16x8 Vec;
+    static constexpr uint32_t kOne2 = 0x3F803F80u;
     static __device__ __forceinline__ f32x4 run(Vec a, Vec b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
@@ -184,15 +186,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15;
     const int q = lane >> 4;
     const int Hq = a.num_heads;
     const int row0 = tile * kRows + wave * 16 * kRB;     // this wave's first row
 
-    // this lane's rows (B-operand column c of each 16-row block)
+    // this lane's rows (B-operand column c of each 16-row block).  Scores
+    // are kept unscaled and the (positive) scale enters in the exponent's
+    // FMA; a negative scale is moved onto the queries as an exact sign flip.
     int pos[kRB];                                        // query positions
     Vec qop[kRB][KSTEPS];
+    const uint32_t qsign = a.score_scale < 0.f ? 0x80008000u : 0u;
+    // (a zero scale is raised to the least normal float, so that a masked
+    // score, -inf, still scales to -inf and not to NaN)
+    const float sscale = fmaxf(fabsf(a.score_scale), 1.17549435e-38f);
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
         const int r = min(row0 + 16 * rb + c, rows - 1);
@@ -201,7 +209,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                              ((int64_t)(first + r / G) * Hq + g * G + r % G) * D + 8 * q;
 #pragma unroll
         for (int k = 0; k < KSTEPS; ++k)
-            qop[rb][k] = __builtin_bit_cast(Vec, *reinterpret_cast<const uint4*>(qp + 32 * k));
+        {
+            uint4 w = *reinterpret_cast<const uint4*>(qp + 32 * k);
+            w.x ^= qsign;
+            w.y ^= qsign;
+            w.z ^= qsign;
+            w.w ^= qsign;
+            qop[rb][k] = __builtin_bit_cast(Vec, w);
+        }
     }
     const int pos_first = L - n + row0 / G;              // the wave's earliest query
     const int last_row = min(tile * kRows + kRows, rows) - 1;
@@ -268,6 +283,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     // ---- K/V tile loads ---------------------------------------------------------
     const int64_t row_bytes = (int64_t)Hkv * D * KB;
+    const uint32_t half_bytes = (uint32_t)(row_bytes << shift);      // the K (or V) half of a block
+    const uint32_t blk_bytes = 2u * half_bytes;
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
 
     // Each thread moves U chunks of K and of V per tile (chunk tid + 256u).
@@ -288,12 +305,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             vd = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.new_value) + src);
             return;
         }
-        int blk = block_of(t);
-        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-        const int64_t krow = ((int64_t)blk * 2 << shift) + (t & (a.block_size - 1));
-        const uint8_t* kp = pool + krow * row_bytes + (int64_t)(g * D + ch * EPC) * KB;
+        uint32_t blk = (uint32_t)block_of(t);
+        blk = blk < (uint32_t)a.num_blocks ? blk : 0u;
+        // a block is at most 4 GiB (checked on the host): 32-bit factors, one 64-bit product
+        const uint32_t inner = (uint32_t)(t & (a.block_size - 1)) * (uint32_t)row_bytes + (uint32_t)((g * D + ch * EPC) * KB);
+        const uint8_t* kp = pool + ((uint64_t)blk * blk_bytes + inner);
         kd = *reinterpret_cast<const uint4*>(kp);
-        vd = *reinterpret_cast<const uint4*>(kp + (row_bytes << shift));
+        vd = *reinterpret_cast<const uint4*>(kp + half_bytes);
     };
     auto load_tile = [&](int kt) {
         Tile r;
@@ -326,17 +344,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
 
     // ---- per-tile math -------------------------------------------------------------
-    float m_run[kRB], l_lane[kRB];   // running max of row c (same in the row's 4 lanes); lane share of the sum
-    f32x4 oacc[kRB][DT];
+    // running max of row c (scaled, the same in the row's 4 lanes); the row
+    // sums come from the matrix cores as P times a column of ones, in the C
+    // layout of o (lane (c, q), register i: row 4q + i)
+    float m_run[kRB];
+    f32x4 oacc[kRB][DT], lacc[kRB];
+    const Vec ones = __builtin_bit_cast(Vec, make_uint4(M::kOne2, M::kOne2, M::kOne2, M::kOne2));
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
         m_run[rb] = -INFINITY;
-        l_lane[rb] = 0.f;
+        lacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < DT; ++t) oacc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto compute = [&](int kt, int buf) {
+    auto compute = [&](int kt, int buf, auto mask_tag) {
+        constexpr bool kMasked = decltype(mask_tag)::value;
         const uint16_t* sk = s_k[buf];
         const uint16_t* sv = s_v[buf];
         // S^T = K Q^T for the tile's two 16-key halves; each K operand serves both row blocks
@@ -353,8 +376,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
         // online softmax (lane: keys 4q+i and 16+4q+i of row c of each block).
-        // Only tiles that reach past the wave's earliest query need the mask.
-        const bool masked = kt * kKeys + kKeys - 1 > pos_first;
+        // Only tiles that reach past the wave's earliest query take the mask.
         Vec pop[kRB], pop_lo[kRB];
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) {
@@ -365,13 +387,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = kt * kKeys + 16 * u + 4 * q + i;
-                    float v = sacc[rb][u][i] * a.score_scale;
-                    if (masked) v = key <= pos[rb] ? v : -INFINITY;
+                    float v = sacc[rb][u][i];
+                    if constexpr (kMasked) v = key <= pos[rb] ? v : -INFINITY;
                     sc[4 * u + i] = v;
                     mx = fmaxf(mx, v);
                 }
             }
-            mx = max_across_rows(mx);
+            mx = max_across_rows(mx) * sscale;
             // The reference max moves only when a row's max grows by more
             // than kSlack (log2 units): the weights stay below 2^kSlack and
             // most tiles need no rescale of o at all.
@@ -379,22 +401,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const float m_new = grow ? mx : m_run[rb];         // finite: key 0 precedes every query
             const float alpha = grow ? fast_exp2(m_run[rb] - m_new) : 1.f;
             uint32_t pw[4], plw[4];     // packed probabilities (k-slot pairs)
-            float psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p0 = fast_exp2(sc[2 * e] - m_new);         // masked: 2^-inf = 0
-                const float p1 = fast_exp2(sc[2 * e + 1] - m_new);
+                const float p0 = fast_exp2(fmaf(sc[2 * e], sscale, -m_new));     // masked: 2^-inf = 0
+                const float p1 = fast_exp2(fmaf(sc[2 * e + 1], sscale, -m_new));
                 pw[e] = M::round2(p0, p1);
-                const float r0 = M::lo(pw[e]), r1 = M::hi(pw[e]);
-                psum += r0;
-                psum += r1;
                 if constexpr (SPLIT) {
+                    const float r0 = M::lo(pw[e]), r1 = M::hi(pw[e]);
                     plw[e] = M::round2(p0 - r0, p1 - r1);              // the differences are exact in fp32
-                    psum += M::lo(plw[e]);
-                    psum += M::hi(plw[e]);
                 }
             }
-            l_lane[rb] = l_lane[rb] * alpha + psum;
             m_run[rb] = m_new;
             if (__builtin_amdgcn_ballot_w64(grow)) {
                 float ar[4];
@@ -405,6 +421,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                     for (int i = 0; i < 4; ++i) oacc[rb][t][i] *= ar[i];
                 }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lacc[rb][i] *= ar[i];
             }
             pop[rb] = __builtin_bit_cast(Vec, make_uint4(pw[0], pw[1], pw[2], pw[3]));
             if constexpr (SPLIT) pop_lo[rb] = __builtin_bit_cast(Vec, make_uint4(plw[0], plw[1], plw[2], plw[3]));
@@ -429,6 +447,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 if constexpr (SPLIT) oacc[rb][t] = M::run(pop_lo[rb], vf, oacc[rb][t]);
             }
         }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            lacc[rb] = M::run(pop[rb], ones, lacc[rb]);
+            if constexpr (SPLIT) lacc[rb] = M::run(pop_lo[rb], ones, lacc[rb]);
+        }
     };
 
     // ---- main loop: two LDS buffers --------------------------------------------
@@ -440,30 +463,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     store_tile(0, tl);
     if (n_tiles > 1) tl = load_tile(1);
     __syncthreads();
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        compute(kt, kt & 1);
+    // Tiles below the wave's earliest query need no mask: they run in a loop
+    // of their own, the rest (at most kRows / kKeys + 1) in a second one.
+    auto step = [&](int kt, auto mask_tag) {
+        compute(kt, kt & 1, mask_tag);
         if (kt + 1 < n_tiles) {
             store_tile((kt + 1) & 1, tl);
             if (kt + 2 < n_tiles) tl = load_tile(kt + 2);
         }
         __syncthreads();
-    }
+    };
+    const int n_plain = min((pos_first + 1) / kKeys, n_tiles);   // tiles with kt * kKeys + kKeys - 1 <= pos_first
+    int kt = 0;
+    for (; kt < n_plain; ++kt) step(kt, MaskTag<false>{});
+    for (; kt < n_tiles; ++kt) step(kt, MaskTag<true>{});
 
     // ---- finish: row sums, normalise, store ----------------------------------
     uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-        float lsum = l_lane[rb];
-        lsum += shfl_xor(lsum, 16);
-        lsum += shfl_xor(lsum, 32);
-        float lr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lr[i] = from_lane(lsum, 4 * q + i);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int R = row0 + 16 * rb + 4 * q + i;
             if (R >= rows) continue;
-            const float inv = a.v_scale / lr[i];
+            const float inv = a.v_scale / lacc[rb][i];
             uint16_t* dst = out + ((int64_t)(first + R / G) * Hq + g * G + R % G) * D + c;
 #pragma unroll
             for (int t = 0; t < DT; ++t) dst[16 * t] = M::round(oacc[rb][t][i] * inv);
