@@ -363,7 +363,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const uint16_t* sk = s_k[buf];
         const uint16_t* sv = s_v[buf];
         // S^T = K Q^T for the tile's two 16-key halves; each K operand serves both row blocks
+        // The matrix-core phases run at raised wave priority, so that a
+        // wave in its softmax leaves the issue slots to the other wave of the
+        // SIMD while that one has MFMAs to issue.
         f32x4 sacc[kRB][2];
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -375,6 +379,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int rb = 0; rb < kRB; ++rb) sacc[rb][u] = M::run(kf, qop[rb][k], sacc[rb][u]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // online softmax (lane: keys 4q+i and 16+4q+i of row c of each block).
         // Only tiles that reach past the wave's earliest query take the mask.
         Vec pop[kRB], pop_lo[kRB];
@@ -434,6 +439,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // group addresses V[4q + j][16t + 4m] (and the same 16 keys on).
         const int tr_key = 4 * q + (c >> 2);
         const int tr_col = 4 * (c & 3);
+        if constexpr (!SPLIT) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -452,6 +458,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             lacc[rb] = M::run(pop[rb], ones, lacc[rb]);
             if constexpr (SPLIT) lacc[rb] = M::run(pop_lo[rb], ones, lacc[rb]);
         }
+        if constexpr (!SPLIT) __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- main loop: two LDS buffers --------------------------------------------
