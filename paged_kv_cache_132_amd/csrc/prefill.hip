@@ -27,9 +27,12 @@
 //         row c, the same head_dim positions, held in registers).  Two
 //         16-key tiles give lane (c, q) the scores of keys 4q+i and 16+4q+i
 //         for row c.
-//   soft  online softmax in the exp2 domain: masked keys (after the row's
-//         position) get weight 0; probabilities are rounded to the MFMA
-//         input type once and the running sum uses the rounded values.
+//   soft  online softmax in the exp2 domain on the unscaled scores (the
+//         scale enters through the exponent's FMA): masked keys (after the
+//         row's position; only the last tiles of a wave take the mask) get
+//         weight 0; probabilities are rounded to the MFMA input type once,
+//         and the running sum, P times a column of ones on the matrix cores,
+//         adds exactly the rounded values.
 //         With bf16 K/V the probability is split into a bf16 part and a bf16
 //         remainder and PV runs on both: one bf16 rounding (2^-9 relative)
 //         of a peaked softmax would otherwise move an output by up to
