@@ -154,6 +154,25 @@ def test_peaked_softmax_precision(qd, kvd):
     assert_decode_close(oracle.to_f64(host_bits(out), qd), ref, b)
 
 
+@pytest.mark.parametrize("scale", [-0.0883883476, 0.0])
+@pytest.mark.parametrize("qd,kvd", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8_e4m3")])
+def test_negative_and_zero_scale(scale, qd, kvd):
+    """The kernel keeps scores unscaled and applies the scale in the
+    exponent: a negative scale is moved onto the queries as a sign flip and a
+    zero scale (every visible key weighs the same) must not turn the masked
+    keys' -inf into NaN.  Both against the oracle's plain softmax."""
+    b = make_prefill("scale_sign", 74, [300, 129, 40], [120, 129, 40], 16, 4, 128, 16, qd, kvd)
+    b.scale = scale
+    pool = _start_pool(b)
+    dev, out = _gpu_prompt(b, pool)
+    want_pool = _oracle_pool(b, pool)
+    ref = oracle.paged_prefill(b.query, qd, want_pool, kvd, b.block_table_array(), b.context_lens,
+                               b.cu_seqlens, 16, b.scale, b.k_scale, b.v_scale)
+    got = oracle.to_f64(host_bits(out), qd)
+    assert np.isfinite(got).all()
+    assert_decode_close(got, ref, b)
+
+
 @pytest.mark.parametrize("kvd", ["f16", "fp8_e4m3"])
 def test_wide_block_tables_read_in_place(kvd):
     """Tables wider than the 2048 entries the kernel stages in LDS take the
