@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             Job j;
             j.src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kvh ? a.new_value : a.new_key) +
                                                    ((int64_t)(first + i) * Hkv + g) * D + c * 8);
-            const int64_t drow = ((int64_t)blk * 2 + kvh << shift) + (t & (a.block_size - 1));
+            const int64_t drow = (((int64_t)blk * 2 + kvh) << shift) + (t & (a.block_size - 1));
             j.dst = (x < total && blk >= 0 && blk < a.num_blocks)
                         ? reinterpret_cast<uint4*>(pool16 + drow * row_elems + g * D + c * 8) : nullptr;
             return j;
