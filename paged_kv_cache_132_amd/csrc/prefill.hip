@@ -242,47 +242,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
 
     // ---- fused prompt-stage write ([CANN notes §4.2]: the prompt kernel
-    // writes K and V as it goes).  This workgroup stores the K and V rows of
-    // head g for the new tokens its own query rows belong to; every
-    // workgroup reads new tokens' K and V from the source rows instead of the
-    // pool, so no workgroup waits for another's stores.
-    if constexpr (WRITE) {
-        constexpr int CPR = D / 8;                          // 16-byte chunks per head row
-        const int i0 = tile * kRows / G;
-        const int i1 = min(n, (tile + 1) * kRows / G);
-        const int total = (i1 - i0) * 2 * CPR;
-        const int64_t row_elems = (int64_t)Hkv * D;
-        uint16_t* pool16 = static_cast<uint16_t*>(const_cast<void*>(a.kv_pool));
-        // chunk x: 16 bytes of the K (or V) row of new token i0 + x / (2 CPR),
-        // head g; past `total` the source is re-read and nothing is stored
-        struct Job {
-            const uint4* src;
-            uint4* dst;
-        };
-        auto job = [&](int x) {
-            const int xc = min(x, total - 1);
-            const int c = xc % CPR;
-            const int kvh = (xc / CPR) & 1;
-            const int i = i0 + xc / (2 * CPR);
-            const int t = L - n + i;
-            const int blk = block_of(t);
-            Job j;
-            j.src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kvh ? a.new_value : a.new_key) +
-                                                   ((int64_t)(first + i) * Hkv + g) * D + c * 8);
-            const int64_t drow = (((int64_t)blk * 2 + kvh) << shift) + (t & (a.block_size - 1));
-            j.dst = (x < total && blk >= 0 && blk < a.num_blocks)
-                        ? reinterpret_cast<uint4*>(pool16 + drow * row_elems + g * D + c * 8) : nullptr;
-            return j;
-        };
-        for (int x0 = tid; x0 < total; x0 += 4 * kThreads) {   // four chunks in flight per thread
-            const Job j0 = job(x0), j1 = job(x0 + kThreads), j2 = job(x0 + 2 * kThreads), j3 = job(x0 + 3 * kThreads);
-            const uint4 w0 = *j0.src, w1 = *j1.src, w2 = *j2.src, w3 = *j3.src;
-            if (j0.dst) *j0.dst = w0;
-            if (j1.dst) *j1.dst = w1;
-            if (j2.dst) *j2.dst = w2;
-            if (j3.dst) *j3.dst = w3;
-        }
-    }
+    // writes K and V as it goes).  This workgroup owns the new tokens its own
+    // query rows belong to, i0 .. i1 - 1; the main loop loads every one of
+    // them (they are its diagonal tiles), and the thread that holds a chunk
+    // of an owned token's K and V stores it into the token's slot when it
+    // moves the tile into LDS.  Every workgroup reads new tokens' K and V
+    // from the source rows, so none waits for another's stores.
+    const int i0 = tile * kRows / G;
+    const int i1 = min(n, (tile + 1) * kRows / G);
 
     // ---- K/V tile loads ---------------------------------------------------------
     const int64_t row_bytes = (int64_t)Hkv * D * KB;
@@ -324,10 +291,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
 
     // K and V both row-major in LDS (fp8 widened to bf16 exactly)
-    auto store_chunk = [&](int buf, int ci, uint4 kc, uint4 vc) {
+    auto store_chunk = [&](int kt, int buf, int ci, uint4 kc, uint4 vc) {
         if (CHUNKS % kThreads != 0 && ci >= CHUNKS) return;
         const int key = ci / CPK;
         const int d0 = (ci % CPK) * EPC;
+        if constexpr (WRITE) {
+            const int t = kt * kKeys + key;              // not clamped: an owned token is < L
+            const int i = t - (L - n);
+            if (i >= i0 && i < i1) {
+                const uint32_t blk = (uint32_t)block_of(t);
+                if (blk < (uint32_t)a.num_blocks) {
+                    const uint32_t inner = (uint32_t)(t & (a.block_size - 1)) * (uint32_t)row_bytes +
+                                           (uint32_t)((g * D + d0) * KB);
+                    uint8_t* kp = const_cast<uint8_t*>(pool) + ((uint64_t)blk * blk_bytes + inner);
+                    *reinterpret_cast<uint4*>(kp) = kc;
+                    *reinterpret_cast<uint4*>(kp + half_bytes) = vc;
+                }
+            }
+        }
         if constexpr (KVT == PA_FP8_E4M3) {
             uint4 klo, khi, vlo, vhi;
             widen16_fp8(kc, klo, khi);
@@ -341,9 +322,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             *reinterpret_cast<uint4*>(&s_v[buf][key * VS + d0]) = vc;
         }
     };
-    auto store_tile = [&](int buf, const Tile& tl) {
-        store_chunk(buf, tid, tl.k0, tl.v0);
-        if constexpr (U > 1) store_chunk(buf, tid + kThreads, tl.k1, tl.v1);
+    auto store_tile = [&](int kt, int buf, const Tile& tl) {
+        store_chunk(kt, buf, tid, tl.k0, tl.v0);
+        if constexpr (U > 1) store_chunk(kt, buf, tid + kThreads, tl.k1, tl.v1);
     };
 
     // ---- per-tile math -------------------------------------------------------------
@@ -470,7 +451,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // into the other buffer and issues the loads of tile kt + 2.  One barrier
     // per tile.
     Tile tl = load_tile(0);
-    store_tile(0, tl);
+    store_tile(0, 0, tl);
     if (n_tiles > 1) tl = load_tile(1);
     __syncthreads();
     // Tiles below the wave's earliest query need no mask: they run in a loop
@@ -478,7 +459,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     auto step = [&](int kt, auto mask_tag) {
         compute(kt, kt & 1, mask_tag);
         if (kt + 1 < n_tiles) {
-            store_tile((kt + 1) & 1, tl);
+            store_tile(kt + 1, (kt + 1) & 1, tl);
             if (kt + 2 < n_tiles) tl = load_tile(kt + 2);
         }
         __syncthreads();
