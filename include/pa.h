@@ -273,7 +273,10 @@ pa_status pa_cache_write_tokens(void* kv_pool, pa_dtype kv_dtype, const void* ke
  *   max_new_tokens  an upper bound on every n_s (sizes the launch grid).
  *   The pool must already hold the new tokens (pa_cache_write_tokens first,
  *   on the same stream).
- * No workspace.  Supported combinations, scales and errors as in pa_decode.
+ * No workspace.  Supported combinations, scales and errors as in pa_decode;
+ * in addition PA_ERR_BAD_SHAPE when one pool block (2 * block_size *
+ * num_kv_heads * head_dim elements) exceeds 4 GiB.  Any finite scale is
+ * accepted, negative and zero included.
  * Sequences with n_s = 0, or with n_s > L_s, produce no output rows.
  */
 pa_status pa_prefill(void* out, const void* query, pa_dtype q_dtype, const void* kv_pool, pa_dtype kv_dtype,

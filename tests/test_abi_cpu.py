@@ -242,6 +242,8 @@ def call_prefill(lib, **kw):
     (dict(head_dim=96), UNSUP),
     (dict(num_heads=24, num_kv_heads=8), UNSUP),
     (dict(kv_dtype=FP8, q_dtype=BF16, k_scale=0.0), SHAPE),
+    # one pool block of 2 x 32 x 300000 x 128 fp16 elements: past 4 GiB
+    (dict(num_heads=300000, num_kv_heads=300000, head_dim=128, block_size=32, num_tokens=1), SHAPE),
 ])
 def test_prefill_rejects_bad_arguments(lib, kw, status):
     assert call_prefill(lib, **kw) == status
