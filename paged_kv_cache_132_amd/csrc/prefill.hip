@@ -42,6 +42,11 @@
 //         copy with ds_read_tr16_b64 (two reads give a lane the 8 keys of one
 //         head_dim column in that k-slot order); head_dim/16 MFMAs per row
 //         block accumulate O[row][d] in fp32.
+//
+// With the write fused (16-bit KV), new tokens' K and V are read from the
+// source rows, and the workgroup that owns a new token (its query rows)
+// stores the token's K and V into its slot from the tile registers of its own
+// main loop; no workgroup reads a slot another one writes.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
