@@ -51,6 +51,7 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
@@ -85,9 +86,14 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
-__device__ __forceinline__ float shfl_xor(float x, int m) {
-    const int lane = __lane_id();
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __builtin_bit_cast(int, x)));
+// max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the 4 rows holding one
+// head), on the VALU: each v_permlane{16,32}_swap with both operands x
+// leaves, in its two results, x of this lane and of lane l ^ 16 (l ^ 32)
+__device__ __forceinline__ float max_across_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float from_lane(float x, int src) {
@@ -121,13 +127,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     }
 
     // ---- query operand: head n of this KV head's group, head_dim 32q.. ----
+    // Scores stay unscaled out of the MFMA and the positive scale enters in
+    // the exponent's FMA; a negative scale is moved onto the queries as an
+    // exact sign flip, and a zero scale is raised to the least normal float
+    // (so a masked -inf score still scales to -inf).
+    const uint32_t qsign = a.score_scale < 0.f ? 0x80008000u : 0u;
+    const float sscale = fmaxf(fabsf(a.score_scale), 1.17549435e-38f);
     bf16x8 qop[4];
     {
         const uint16_t* qp = static_cast<const uint16_t*>(a.query) + ((int64_t)s * Hq + g * G + (n < G ? n : 0)) * kD + 16 * q;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int d0 = (c >> 1) * 64 + (c & 1) * 8;
-            const uint4 v = n < G ? *reinterpret_cast<const uint4*>(qp + d0) : make_uint4(0, 0, 0, 0);
+            uint4 v = n < G ? *reinterpret_cast<const uint4*>(qp + d0) : make_uint4(0, 0, 0, 0);
+            v.x ^= qsign;
+            v.y ^= qsign;
+            v.z ^= qsign;
+            v.w ^= qsign;
             qop[c] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -150,7 +166,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     const uint32_t tr_off = (uint32_t)((16 * (jj >> 2) + 4 * q + (jj & 3)) * kRowStride + 8 * (lane & 1));
 
     float m_run = -INFINITY;       // running max of head n (identical in all 4 rows)
-    float l_lane = 0.f;            // this lane's share of head n's running sum
+    // running sums as P times a column of ones on the matrix cores, in the C
+    // layout of O (register i: head 4q + i)
+    f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
     f32x4 oacc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -256,20 +275,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
                 sacc[u] = acc;
             }
             // online softmax over the step's 32 tokens (lane: tokens 4q+i of each half, head n)
+            // Only a step that reaches past the segment, or holds a dropped
+            // half, takes the mask (a uniform branch).
             float sc[8];
-            float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tt = t0 + 16 * u + 4 * q + i;
-                    const float v = (half_ok[u] && tt < seg_t1) ? sacc[u][i] * a.score_scale : -INFINITY;
-                    sc[4 * u + i] = v;
-                    mx = fmaxf(mx, v);
+                for (int i = 0; i < 4; ++i) sc[4 * u + i] = sacc[u][i];
+            }
+            if (!(half_ok[0] && half_ok[1] && t0 + kStepTokens <= seg_t1)) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tt = t0 + 16 * u + 4 * q + i;
+                        if (!(half_ok[u] && tt < seg_t1)) sc[4 * u + i] = -INFINITY;
+                    }
                 }
             }
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
+            float mx = sc[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+            mx = max_across_rows(mx) * sscale;
             // The reference max moves only when a head's max grows by more
             // than kSlack (log2 units): weights stay below 2^kSlack and most
             // steps skip the rescale of O (an AGPR round trip).  A step whose
@@ -277,16 +304,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
             const bool grow = mx > m_run + kSlack;
             const float m_new = grow ? mx : m_run;
             const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-            // probabilities rounded to bf16 once: the same values feed the PV
-            // product and the running sum, so the weights normalise exactly
-            uint16_t pb[8];
-            float psum = 0.f;
+            const float m_sub = m_new == -INFINITY ? 0.f : m_new;   // no finite score yet: every weight is 0
+            // probabilities rounded to bf16 once (RNE, in pairs): the same
+            // values feed the PV product and the running sum, so the weights
+            // normalise exactly
+            uint32_t pw[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pb[e] = bf16_bits(sc[e] == -INFINITY ? 0.f : fast_exp2(sc[e] - m_new));
-                psum += __uint_as_float((uint32_t)pb[e] << 16);
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(fmaf(sc[2 * e], sscale, -m_sub));      // masked: 2^-inf = 0
+                const float p1 = fast_exp2(fmaf(sc[2 * e + 1], sscale, -m_sub));
+                pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
             }
-            l_lane = l_lane * alpha + psum;
             m_run = m_new;
             // rescale O rows (head 4q+i in register i) when some real head's max moved
             if (__builtin_amdgcn_ballot_w64(n < G && grow)) {
@@ -298,11 +326,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
 #pragma unroll
                     for (int i = 0; i < 4; ++i) oacc[t][i] *= ar[i];
                 }
-            }
-            // PV
-            bf16x8 pop;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pop[e] = __builtin_bit_cast(__bf16, pb[e]);
+                for (int i = 0; i < 4; ++i) lacc[i] *= ar[i];
+            }
+            // PV, and the row sums
+            const bf16x8 pop = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+            lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, ones, lacc, 0, 0, 0);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -327,13 +356,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     }
 
     // ---- finish: per-head sums, then the output or a split-K partial -------
-    l_lane += shfl_xor(l_lane, 16);
-    l_lane += shfl_xor(l_lane, 32);
     const int P = a.max_partitions;
     float lr[4], mr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        lr[i] = from_lane(l_lane, 4 * q + i);
+        lr[i] = lacc[i];
         mr[i] = from_lane(m_run, 4 * q + i);
     }
 #pragma unroll

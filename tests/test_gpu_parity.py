@@ -91,6 +91,18 @@ def test_small_case(name):
     _run_case(b, partition_sizes=(0, bs, 2 * bs, 64 if bs <= 16 else 96, b.max_blocks_per_seq * bs))
 
 
+@pytest.mark.parametrize("scale", [-0.0883883476, 0.0])
+@pytest.mark.parametrize("case", ["mha_f16_d128_bs16", "gqa4_fp8_d128_bs16", "gqa8_bf16_d64_partial_group"])
+def test_negative_and_zero_scale(case, scale):
+    """Any finite softmax scale: the matrix-core kernel keeps scores unscaled
+    and applies the scale in the exponent (a negative scale moved onto the
+    queries, a zero scale giving the plain mean of the visible V rows)."""
+    lens, hq, hkv, d, bs, qd, kvd = SMALL_CASES[case]
+    b = make_custom(case, 140 + sorted(SMALL_CASES).index(case), lens, hq, hkv, d, bs, qd, kvd)
+    b.scale = scale
+    _run_case(b, partition_sizes=(0, bs))
+
+
 def test_zero_and_one_token_sequences():
     b = make_custom("edge", 7, [0, 1, 18, 0, 1], 8, 8, 128, 16, "f16", "f16")
     bt, lens = b.block_table_array(pad=0), b.context_lens
