@@ -65,16 +65,17 @@ def algorithmic_bytes(b) -> dict:
     return {"kv": kv, "decode": decode, "write": write, "unique_kv_blocks": unique_kv}
 
 
-# the sources the decode kernels and their launcher are built from
+# the sources the decode kernels and their launcher are built from, and the
+# build script whose compiler flags shape the code too
 DECODE_SOURCES = ("decode.hip", "decode_gqa_mfma.hip", "decode_common.h", "kv_encode.h", "pa_internal.h",
-                  "pa_api.cpp")
+                  "pa_api.cpp", "../build.py")
 
 
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(REPO, "paged_kv_cache_132_amd", "csrc")
     for name in DECODE_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.normpath(os.path.join(csrc, name)), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 

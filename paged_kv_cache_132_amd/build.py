@@ -37,6 +37,9 @@ def _compile(sources, out, verbose):
         hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-x", "hip",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: with AGPR accumulators the compiler moves
+        # them through VGPRs around every rescale (the fp8 GQA decode kernel)
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wno-unused-command-line-argument",
         f"-I{INCLUDE}", f"-I{CSRC}",
         *[os.path.join(CSRC, s) for s in sources],

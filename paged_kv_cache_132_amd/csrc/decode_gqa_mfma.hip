@@ -404,7 +404,15 @@ int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int grou
         case 8: kernel = w ? decode_gqa_fp8_mfma_kernel<8, true> : decode_gqa_fp8_mfma_kernel<8, false>; break;
         default: return (int)hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+    // Two waves per SIMD: built with VGPR accumulators the kernel needs about
+    // 156 VGPRs, which would admit three, and three measured slower (the
+    // in-flight loads of two waves already cover the latency, a third adds
+    // contention).  Unused dynamic LDS caps a CU at two workgroups.
+    constexpr size_t kStaticLds = (size_t)kDecodeWaves * 2 * kStepTokens * kRowStride;
+    constexpr size_t kCapLds = 18432;
+    static_assert(3 * (kStaticLds + kCapLds) > 160 * 1024 && 2 * (kStaticLds + kCapLds) <= 160 * 1024,
+                  "two workgroups of LDS per CU, not three");
+    hipLaunchKernelGGL(kernel, grid, block, kCapLds, st, a);
     return (int)hipGetLastError();
 }
 
