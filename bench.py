@@ -80,17 +80,17 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(config: str, partition: int, fused: bool):
+def counter_traffic(config: str, partition: int, fused: bool, run_size: int = 1):
     """HBM bytes per attention launch from committed rocprofv3 counter runs, if
     they were taken on the current decode sources, partition and step form
-    (cache write fused or separate); otherwise None."""
+    (cache write fused or separate, shared runs); otherwise None."""
     path = os.path.join(REPO, "profiles", f"decode_{config}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if (rec.get("source_hash") != source_hash() or rec.get("partition") != partition
-            or rec.get("fused_write", False) != fused):
+            or rec.get("fused_write", False) != fused or rec.get("run_size", 1) != run_size):
         return None
     return rec.get("attention_hbm_bytes_per_launch")
 
@@ -445,6 +445,9 @@ def run_decode(args, torch, pa, b) -> dict:
     stream = torch.cuda.current_stream()
 
     fused = not args.separate_write and b.q_dtype == b.src_dtype
+    run_size = int(args.run_size)
+    if run_size != 1 and not fused:
+        raise SystemExit("--run-size takes the fused step (pa_decode_write_partials_shared)")
 
     def step(i, ev=None):
         # one pass of the hot path: cache write, attention pass, split-K merge.
@@ -460,7 +463,7 @@ def run_decode(args, torch, pa, b) -> dict:
         if ev is not None:
             ev[1].record(stream)
         if fused:
-            pa.decode(*dargs, phase="partials", new_key=dev["k"], new_value=dev["v"], **dkw)
+            pa.decode(*dargs, phase="partials", new_key=dev["k"], new_value=dev["v"], run_size=run_size, **dkw)
         else:
             pa.decode(*dargs, phase="partials", **dkw)
         if ev is not None:
@@ -543,7 +546,7 @@ def run_decode(args, torch, pa, b) -> dict:
         f"{'write fused' if fused else f'write {write_ms.mean() * 1e3:.1f} us'}; eager step "
         f"{eager_ms_step * 1e3:.1f} us; graph step "
         f"{'-' if graph_ms_step is None else f'{graph_ms_step * 1e3:.1f}'} us")
-    traffic = counter_traffic(b.name, partition, fused)
+    traffic = counter_traffic(b.name, partition, fused, run_size)
     achievable = stream_read_gbs(torch)
     log(f"streaming-read kernel reaches {achievable:.0f} GB/s on this device")
 
@@ -564,12 +567,14 @@ def run_decode(args, torch, pa, b) -> dict:
             "workload": b.name, "num_seqs": b.num_seqs, "num_heads": b.num_heads,
             "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
             "q_dtype": b.q_dtype, "kv_dtype": b.kv_dtype, "context_tokens": int(b.context_lens.sum()),
-            "seed": b.seed, "partition_size": partition, "pool_copies": copies,
+            "seed": b.seed, "partition_size": partition, "pool_copies": copies, "run_size": run_size,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_launch": "hip_graph" if graph_ms_step is not None else "eager",
         "warm_ms_per_step": round(warm_ms_step, 4) if graph_ms_step is not None else None,
-        "step_kernels": ("pa_decode_write_partials (cache write fused), pa_decode_merge" if fused else
+        "step_kernels": (f"pa_decode_write_partials_shared (runs of {run_size}, cache write fused), "
+                         "pa_decode_merge" if run_size != 1 else
+                         "pa_decode_write_partials (cache write fused), pa_decode_merge" if fused else
                          "pa_cache_write, pa_decode_partials, pa_decode_merge"),
         "eager_ms_per_step": round(eager_ms_step, 4),
         "decode_tokens_per_s_per_layer": round(b.num_seqs / (ms_step * 1e-3), 1),
@@ -717,6 +722,9 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--run-size", type=int, default=1,
+                    help="decode step: sequences share prefix blocks in aligned runs of this many "
+                         "(pa_decode_write_partials_shared; 1, 2, 4 or 8)")
     ap.add_argument("--separate-write", action="store_true",
                     help="run pa_cache_write as its own launch instead of fusing it into the attention pass")
     ap.add_argument("--eager", action="store_true",

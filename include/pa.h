@@ -233,6 +233,47 @@ pa_status pa_decode_write_partials(void* out, const void* query, pa_dtype q_dtyp
                                    void* stream, const void* key, const void* value, pa_dtype src_dtype);
 
 /*
+ * pa_decode_shared, pa_decode_write_partials_shared -- pa_decode and
+ * pa_decode_write_partials for batches whose sequences share prefix blocks
+ * in aligned runs ([nano-vllm blog §3, §4.3]: prefix caching and fork map
+ * several sequences' leading logical blocks to one physical block).
+ *
+ *   run_size   1 (no runs: exactly pa_decode / pa_decode_write_partials), 2,
+ *              4 or 8 (else PA_ERR_UNSUPPORTED; < 1: PA_ERR_BAD_SHAPE).
+ *              Sequences run_size*k .. run_size*k + run_size - 1 form run
+ *              k; a trailing incomplete run has no shared partitions.
+ *
+ * A split-K partition that every sequence of a run holds whole, with at
+ * least one token after it, and whose blocks the run's tables map to the
+ * same physical blocks, is computed once for the run: one pass reads each
+ * K/V row once and keeps a softmax state per sequence.  The table contents
+ * decide this on the device, so any run_size gives the same results up to
+ * float rounding order -- runs that share nothing cost only the check.  The
+ * run form applies where num_heads == num_kv_heads (the vector kernel);
+ * otherwise run_size is checked and ignored.  Arguments, workspace (sized by
+ * pa_decode_workspace_size), results and errors are otherwise those of
+ * pa_decode / pa_decode_write_partials, and pa_decode_merge completes
+ * pa_decode_write_partials_shared.
+ */
+pa_status pa_decode_shared(void* out, const void* query, pa_dtype q_dtype,
+                           const void* kv_pool, pa_dtype kv_dtype,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, float scale, float k_scale, float v_scale,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           void* stream, int32_t run_size);
+pa_status pa_decode_write_partials_shared(void* out, const void* query, pa_dtype q_dtype,
+                                          const void* kv_pool, pa_dtype kv_dtype,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                          int32_t num_blocks, float scale, float k_scale, float v_scale,
+                                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                          void* stream, const void* key, const void* value, pa_dtype src_dtype,
+                                          int32_t run_size);
+
+/*
  * pa_cache_write_tokens -- the prompt-stage write: put a packed run of new
  * tokens per sequence into the pool ([CANN notes §3.1] packed layout,
  * [CANN notes §4.2] prompt write into block offsets; [nano-vllm blog §4.3]

@@ -22,7 +22,8 @@ STATUS_NAMES = {
     8: "PA_ERR_POOL_EXHAUSTED", 9: "PA_ERR_UNKNOWN_SEQUENCE",
 }
 EXPORTED = ("pa_cache_write", "pa_cache_write_tokens", "pa_copy_blocks", "pa_decode", "pa_decode_partials",
-            "pa_decode_merge", "pa_decode_write", "pa_decode_write_partials", "pa_decode_workspace_size",
+            "pa_decode_merge", "pa_decode_write", "pa_decode_write_partials", "pa_decode_shared",
+            "pa_decode_write_partials_shared", "pa_decode_workspace_size",
             "pa_decode_partition_size", "pa_prefill", "pa_prefill_write", "pa_status_string",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
             "pa_bm_free_sequence", "pa_bm_take_copies", "pa_bm_sequence_length", "pa_bm_block_table",
@@ -62,6 +63,10 @@ def load() -> ctypes.CDLL:
         for fn in (lib.pa_decode_write, lib.pa_decode_write_partials):
             fn.restype = ctypes.c_int
             fn.argtypes = lib.pa_decode.argtypes + [vp, vp, ctypes.c_int]
+        lib.pa_decode_shared.restype = ctypes.c_int
+        lib.pa_decode_shared.argtypes = lib.pa_decode.argtypes + [i32]
+        lib.pa_decode_write_partials_shared.restype = ctypes.c_int
+        lib.pa_decode_write_partials_shared.argtypes = lib.pa_decode_write_partials.argtypes + [i32]
         lib.pa_decode_workspace_size.restype = sz
         lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
         lib.pa_decode_partition_size.restype = i32
@@ -280,14 +285,18 @@ def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tenso
            context_lens: torch.Tensor, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
            out: torch.Tensor | None = None, workspace: torch.Tensor | Workspace | None = None,
            partition_size: int = 0, stream=None, phase: str = "both",
-           new_key: torch.Tensor | None = None, new_value: torch.Tensor | None = None) -> torch.Tensor:
+           new_key: torch.Tensor | None = None, new_value: torch.Tensor | None = None,
+           run_size: int = 1) -> torch.Tensor:
     """Paged decode attention; returns out [num_seqs, num_heads, head_dim] of query's dtype.
 
     phase: "both" (pa_decode), "partials" (pa_decode_partials) or "merge"
     (pa_decode_merge, with the same arguments and workspace as the partials call).
     new_key / new_value ([num_seqs, num_kv_heads, head_dim], query dtype): write
     each sequence's newest token in the same pass (pa_decode_write /
-    pa_decode_write_partials), as pa_cache_write would."""
+    pa_decode_write_partials), as pa_cache_write would.
+    run_size > 1: sequences share prefix blocks in aligned runs of that many
+    (pa_decode_shared with phase "both", pa_decode_write_partials_shared with
+    new_key / new_value and phase "partials")."""
     nb, bs, hkv, d = _pool_dims(kv_pool)
     if query.dim() != 3 or query.shape[2] != d or not query.is_contiguous():
         raise ValueError("query must be a contiguous [num_seqs, num_heads, head_dim] tensor")
@@ -306,9 +315,15 @@ def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tenso
     else:
         ws = workspace
     extra = ()
+    if run_size != 1 and phase != "merge":
+        if (new_key is None) != (phase == "both"):
+            raise ValueError("run_size: pa_decode_shared (phase 'both', no write) or "
+                             "pa_decode_write_partials_shared (phase 'partials' with new_key / new_value)")
     if new_key is None:
         fn = {"both": load().pa_decode, "partials": load().pa_decode_partials,
               "merge": load().pa_decode_merge}[phase]
+        if run_size != 1 and phase == "both":
+            fn, extra = load().pa_decode_shared, (int(run_size),)
     else:
         if phase == "merge":
             raise ValueError("the fused write belongs to the attention pass, not the merge")
@@ -317,6 +332,8 @@ def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tenso
             raise ValueError("new_key/new_value must be contiguous [num_seqs, num_kv_heads, head_dim] of one dtype")
         fn = {"both": load().pa_decode_write, "partials": load().pa_decode_write_partials}[phase]
         extra = (_ptr(new_key), _ptr(new_value), pa_dtype(new_key))
+        if run_size != 1:
+            fn, extra = load().pa_decode_write_partials_shared, extra + (int(run_size),)
     st = fn(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), kvt,
             _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, mb, nb,
             float(scale), float(k_scale), float(v_scale), int(partition_size),

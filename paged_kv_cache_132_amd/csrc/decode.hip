@@ -165,8 +165,12 @@ __device__ __forceinline__ void accumulate_v(float (&o)[EPL], float p, const uin
 template <int QT, int D, int NE>
 __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h, int d0, int n_part);
 
-template <int QT, int KVT, int D, int G, bool WRITE>
+// RUN: the run kernel.  G is then the run length: "query head" gi of KV
+// head g is head g of sequence s + gi (num_heads == num_kv_heads), and the
+// workgroup's partition is one its run shares, read once for all of them.
+template <int QT, int KVT, int D, int G, bool WRITE, bool RUN = false>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
+    static_assert(!(RUN && WRITE), "a shared partition never holds a newest token");
     constexpr int KVB = KVT == PA_FP8_E4M3 ? 1 : 2;
     constexpr int ROWL = D * KVB / 16;      // lanes per KV-head row
     constexpr int ROWS = 64 / ROWL;         // KV heads per workgroup
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 
     // ---- which (sequence, KV-head group, partition) -------------------------
     WorkItem w;
-    if (!find_work(a, blockIdx.x, w)) return;
+    if (!(RUN ? find_run_work(a, blockIdx.x, w) : find_work(a, blockIdx.x, w))) return;
     const int s = w.s, p = w.p, group = w.group, L = w.L, n_part = w.n_part;
 
     const int tid = threadIdx.x;
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int Hq = a.num_heads;
     uint16_t* out = static_cast<uint16_t*>(a.out);
 
-    if (L <= 0) {                                          // empty sequence: zero output
+    if (!RUN && L <= 0) {                                  // empty sequence: zero output
         if (wave == 0 && row_ok) {
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) {
@@ -210,14 +214,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
 
     // ---- query slices of the G query heads that read KV head g ------------
+    // (RUN: head g of the run's G sequences)
     uint32_t q[G][QDW];
     {
-        const uint16_t* qb = static_cast<const uint16_t*>(a.query) + ((int64_t)s * Hq + g * G) * D + j * EPL;
+        const uint16_t* qb = static_cast<const uint16_t*>(a.query) + ((int64_t)s * Hq + g * (RUN ? 1 : G)) * D + j * EPL;
+        const int64_t qstride = RUN ? (int64_t)Hq * D : D;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
 #pragma unroll
             for (int w = 0; w < QDW; w += 4) {
-                const uint4 v = *reinterpret_cast<const uint4*>(qb + gi * D + 2 * w);
+                const uint4 v = *reinterpret_cast<const uint4*>(qb + gi * qstride + 2 * w);
                 q[gi][w] = v.x; q[gi][w + 1] = v.y; q[gi][w + 2] = v.z; q[gi][w + 3] = v.w;
             }
         }
@@ -320,7 +326,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         const int my_blk = in_seg ? bt_row[seg0 + lane] : 0;
         const int prev_blk = in_seg && s > 0 ? bt_row[seg0 + lane - a.max_blocks_per_seq] : -1;
         const int next_blk = in_seg && s + 1 < a.num_seqs ? bt_row[seg0 + lane + a.max_blocks_per_seq] : -1;
-        const uint64_t shared = __builtin_amdgcn_ballot_w64(in_seg && (my_blk == prev_blk || my_blk == next_blk));
+        // (the run kernel reads each block once: streamed)
+        const uint64_t shared = RUN ? 0ull : __builtin_amdgcn_ballot_w64(in_seg && (my_blk == prev_blk || my_blk == next_blk));
         const int seg_t0 = max(t_begin, seg0 << shift);
         const int seg_t1 = min(t_end, (seg0 + seg_blocks) << shift);
         const int n_chunks = (seg_t1 - seg_t0 + TPC - 1) / TPC;
@@ -405,16 +412,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
             for (int w = 0; w < NW; ++w) x = fmaf(fw[w], s_o[w][ln * EPL + part * OPT + e], x);
             acc[e] = x;
         }
-        const int h = mg_row * G + gi;
+        const int h = RUN ? mg_row : mg_row * G + gi;
+        const int so = RUN ? s + gi : s;                  // the output's sequence
         const int d0 = mj * EPL + part * OPT;
         if (m_ok) {
             if (n_part == 1) {
                 const float inv = a.v_scale / Lsum;
-                uint16_t* dst = out + ((int64_t)s * Hq + h) * D + d0;
+                uint16_t* dst = out + ((int64_t)so * Hq + h) * D + d0;
 #pragma unroll
                 for (int e = 0; e < OPT; ++e) dst[e] = to_out_bits<QT>(acc[e] * inv);
             } else {
-                const int64_t slot = ((int64_t)s * Hq + h) * P + p;
+                const int64_t slot = ((int64_t)so * Hq + h) * P + p;
                 float* po = a.part_o + slot * D + d0;
 #pragma unroll
                 for (int e = 0; e < OPT; ++e) po[e] = acc[e];
@@ -493,6 +501,30 @@ int launch_d(const DecodeArgs& a, const DecodePlan& plan, int group_size, hipStr
     return (int)hipGetLastError();
 }
 
+// the run kernel: one workgroup per (run, KV-head group, partition); those
+// whose partition the run does not share leave at once
+template <int QT, int KVT, int D>
+int launch_run(const DecodeArgs& a, hipStream_t st) {
+    const int64_t grid = (int64_t)(a.num_seqs / a.share_run) * a.groups * a.max_partitions;
+    if (grid == 0) return 0;
+    if (grid > INT32_MAX) return (int)hipErrorInvalidValue;
+    void (*kernel)(DecodeArgs);
+    switch (a.share_run) {
+        case 2: kernel = decode_kernel<QT, KVT, D, 2, false, true>; break;
+        case 4: kernel = decode_kernel<QT, KVT, D, 4, false, true>; break;
+        case 8: kernel = decode_kernel<QT, KVT, D, 8, false, true>; break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecodeThreads), 0, st, a);
+    return (int)hipGetLastError();
+}
+
+template <int QT, int KVT>
+int launch_run_t(const DecodeArgs& a, int head_dim, hipStream_t st) {
+    if (head_dim == 64) return launch_run<QT, KVT, 64>(a, st);
+    return launch_run<QT, KVT, 128>(a, st);
+}
+
 template <int QT, int D>
 int launch_merge(const DecodeArgs& a, hipStream_t st) {
     const int chunks = (a.num_heads + kDecodeThreads / D - 1) / (kDecodeThreads / D);
@@ -514,6 +546,12 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
     if (plan.grid == 0) return 0;
     int err = 0;
     if (phases & kPhasePartials) {
+        if (a.share_run > 1) {             // the runs' shared partitions first (vector path, one query head per KV head)
+            if (kv_dtype == PA_F16) err = launch_run_t<PA_F16, PA_F16>(a, head_dim, st);
+            else if (kv_dtype == PA_BF16) err = launch_run_t<PA_BF16, PA_BF16>(a, head_dim, st);
+            else err = launch_run_t<PA_BF16, PA_FP8_E4M3>(a, head_dim, st);
+            if (err != 0) return err;
+        }
         if (plan.geo.mfma) err = launch_decode_gqa_mfma(a, plan, group_size, stream);
         else if (kv_dtype == PA_F16) err = launch_t<PA_F16, PA_F16>(a, plan, head_dim, group_size, st);
         else if (kv_dtype == PA_BF16) err = launch_t<PA_BF16, PA_BF16>(a, plan, head_dim, group_size, st);

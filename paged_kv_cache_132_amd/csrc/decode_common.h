@@ -51,6 +51,33 @@ __device__ inline bool batch_shares_prefix(const DecodeArgs& a) {
     return shared;
 }
 
+// Whether run k (sequences R*k .. R*k + R - 1, R = a.share_run) shares
+// partition p: every sequence of the run holds the partition whole with at
+// least one token after it (so neither the newest token nor a ragged tail
+// falls into it) and maps each of its blocks to the run leader's physical
+// block.  Each wave computes it on its own from the tables; all waves agree.
+__device__ inline bool run_shares_partition(const DecodeArgs& a, int k, int p) {
+    const int R = a.share_run;
+    const int s0 = k * R;
+    if (R < 2 || s0 + R > a.num_seqs) return false;
+    const int shift = a.block_shift;
+    const int max_tokens = a.max_blocks_per_seq << shift;
+    const int t1 = (p + 1) * a.partition;          // end of partition p
+    if (t1 >= max_tokens) return false;            // no token can follow it in any table
+    const int lane = threadIdx.x & 63;
+    bool ok = true;
+    if (lane < R) ok = a.context_lens[s0 + lane] > t1;
+    const int b0 = (p * a.partition) >> shift;
+    const int nb = a.partition >> shift;
+    const int MB = a.max_blocks_per_seq;
+    const int32_t* lead = a.block_tables + (int64_t)s0 * MB;
+    for (int x = lane; x < (R - 1) * nb; x += 64) {
+        const int i = 1 + x / nb, jb = b0 + x % nb;
+        ok = ok && lead[(int64_t)i * MB + jb] == lead[jb];
+    }
+    return __builtin_amdgcn_ballot_w64(!ok) == 0;
+}
+
 // Map workgroup `wg` to the wg-th live work item.
 //
 // Items are (sequence s, partition p < items(s), KV-head group) with
@@ -107,7 +134,10 @@ __device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
     if (wg >= total) return false;                // past the last item
     const int x = wg % kXcds, j = wg / kXcds;
     const int per = total / kXcds, rem = total % kXcds;
-    const int item = x * per + min(x, rem) + j;
+    // (with shared runs the per-sequence kernel skips the runs' shared
+    // partitions, a contiguous range of items: dealt round-robin, the live
+    // items still reach every XCD)
+    const int item = a.share_run > 1 ? wg : x * per + min(x, rem) + j;
     const int k = item / a.groups;                // item index ignoring the group
     int lo = 0, hi = P;                           // C(lo) <= k < C(hi)
     while (hi - lo > 1) {
@@ -148,6 +178,25 @@ __device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
     w.group = group;
     w.L = min(a.context_lens[s_found], max_tokens);
     w.n_part = w.L > 0 ? (w.L + a.partition - 1) / a.partition : 0;
+    // a partition a shared run holds is the run kernel's
+    if (a.share_run > 1 && run_shares_partition(a, s_found / a.share_run, p)) return false;
+    return true;
+}
+
+// Map workgroup `wg` of the run kernel to (run k, KV-head group, partition p):
+// group fastest, then run, then partition.  False when that partition is not
+// shared by the run (the per-sequence kernel computes it) or past the grid.
+__device__ inline bool find_run_work(const DecodeArgs& a, int wg, WorkItem& w) {
+    const int runs = a.num_seqs / a.share_run;
+    const int group = wg % a.groups;
+    const int k = (wg / a.groups) % runs;
+    const int p = wg / (a.groups * runs);
+    if (p >= a.max_partitions || !run_shares_partition(a, k, p)) return false;
+    w.s = k * a.share_run;
+    w.p = p;
+    w.group = group;
+    w.L = min(a.context_lens[w.s], a.max_blocks_per_seq << a.block_shift);
+    w.n_part = (w.L + a.partition - 1) / a.partition;
     return true;
 }
 

@@ -397,12 +397,14 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                     float scale, float k_scale, float v_scale, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, void* stream,
-                    const void* new_key = nullptr, const void* new_value = nullptr) {
+                    const void* new_key = nullptr, const void* new_value = nullptr, int32_t run_size = 1) {
     pa_status st = check_decode_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables,
                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                                      block_size, max_blocks_per_seq, num_blocks, scale, k_scale,
                                      v_scale, partition_size);
     if (st != PA_OK) return st;
+    if (run_size < 1) return PA_ERR_BAD_SHAPE;
+    if (run_size != 1 && run_size != 2 && run_size != 4 && run_size != 8) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     DecodePlan plan;
     if (!plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
@@ -438,6 +440,8 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
     a.new_value = new_value;
     a.write_k_scale = k_scale;
     a.write_v_scale = v_scale;
+    // shared runs go to the vector kernel's run form: one query head per KV head
+    a.share_run = (run_size > 1 && !plan.geo.mfma && num_heads == num_kv_heads) ? run_size : 0;
     const int err = launch_decode(a, plan, q_dtype, kv_dtype, head_dim, num_heads / num_kv_heads,
                                   phases, stream);
     return err == 0 ? PA_OK : PA_ERR_HIP;
@@ -459,15 +463,22 @@ pa_status pa_decode_partials(PA_DECODE_PARAMS) { return decode_phases(kPhasePart
 pa_status pa_decode_merge(PA_DECODE_PARAMS) { return decode_phases(kPhaseMerge, PA_DECODE_ARGS); }
 
 // pa_decode with the newest tokens' K/V written by the attention pass itself
-static pa_status decode_write_phases(int phases, PA_DECODE_PARAMS, const void* key, const void* value,
-                                     pa_dtype src_dtype) {
+static pa_status check_write_source(int32_t num_seqs, pa_dtype q_dtype, const void* key, const void* value,
+                                    pa_dtype src_dtype) {
     if (!known_dtype(src_dtype)) return PA_ERR_BAD_DTYPE;
     if (src_dtype != q_dtype) return PA_ERR_UNSUPPORTED;         // the fused write takes query-dtype rows
     if (num_seqs > 0) {
         if (!key || !value) return PA_ERR_NULL_POINTER;
         if (!aligned16(key) || !aligned16(value)) return PA_ERR_MISALIGNED;
     }
-    return decode_phases(phases, PA_DECODE_ARGS, key, value);
+    return PA_OK;
+}
+
+static pa_status decode_write_phases(int phases, PA_DECODE_PARAMS, const void* key, const void* value,
+                                     pa_dtype src_dtype, int32_t run_size = 1) {
+    const pa_status st = check_write_source(num_seqs, q_dtype, key, value, src_dtype);
+    if (st != PA_OK) return st;
+    return decode_phases(phases, PA_DECODE_ARGS, key, value, run_size);
 }
 
 pa_status pa_decode_write(PA_DECODE_PARAMS, const void* key, const void* value, pa_dtype src_dtype) {
@@ -475,6 +486,14 @@ pa_status pa_decode_write(PA_DECODE_PARAMS, const void* key, const void* value, 
 }
 pa_status pa_decode_write_partials(PA_DECODE_PARAMS, const void* key, const void* value, pa_dtype src_dtype) {
     return decode_write_phases(kPhasePartials, PA_DECODE_ARGS, key, value, src_dtype);
+}
+
+pa_status pa_decode_shared(PA_DECODE_PARAMS, int32_t run_size) {
+    return decode_phases(kPhasePartials | kPhaseMerge, PA_DECODE_ARGS, nullptr, nullptr, run_size);
+}
+pa_status pa_decode_write_partials_shared(PA_DECODE_PARAMS, const void* key, const void* value, pa_dtype src_dtype,
+                                          int32_t run_size) {
+    return decode_write_phases(kPhasePartials, PA_DECODE_ARGS, key, value, src_dtype, run_size);
 }
 
 }  // extern "C"

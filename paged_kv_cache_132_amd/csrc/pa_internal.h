@@ -75,6 +75,12 @@ struct DecodeArgs {
     const void* new_key;
     const void* new_value;
     float write_k_scale, write_v_scale;
+    // Shared runs (0 or 1: none): sequences share_run*k .. share_run*k +
+    // share_run - 1 form run k.  A partition that every sequence of a run
+    // holds whole (with tokens after it) and maps to the same physical blocks
+    // is computed once for the run by the run kernel; the per-sequence
+    // kernel skips it.
+    int32_t share_run;
 };
 
 struct WriteArgs {

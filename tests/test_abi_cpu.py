@@ -107,6 +107,25 @@ def test_decode_zero_sequences_is_a_noop(lib):
     assert call_decode(lib, num_seqs=0, out=None, query=None, workspace=None) == OK
 
 
+def call_decode_shared(lib, run_size, **kw):
+    a = decode_args(**kw)
+    return lib.pa_decode_shared(a["out"], a["query"], a["q_dtype"], a["kv_pool"], a["kv_dtype"],
+                                a["block_tables"], a["context_lens"], a["num_seqs"], a["num_heads"],
+                                a["num_kv_heads"], a["head_dim"], a["block_size"], a["max_blocks_per_seq"],
+                                a["num_blocks"], a["scale"], a["k_scale"], a["v_scale"],
+                                a["partition_size"], a["workspace"], a["workspace_bytes"], a["stream"], run_size)
+
+
+@pytest.mark.parametrize("run_size,status", [(0, SHAPE), (-2, SHAPE), (3, UNSUP), (16, UNSUP)])
+def test_decode_shared_rejects_run_sizes(lib, run_size, status):
+    assert call_decode_shared(lib, run_size) == status
+
+
+def test_decode_shared_checks_the_decode_arguments_first(lib):
+    assert call_decode_shared(lib, 2, out=None) == NULLP
+    assert call_decode_shared(lib, 8, num_seqs=0, out=None, query=None, workspace=None) == OK
+
+
 def call_write(lib, **kw):
     a = dict(kv_pool=FAKE, kv_dtype=F16, key=FAKE, value=FAKE, src_dtype=F16, block_tables=FAKE,
              context_lens=FAKE, num_seqs=4, num_kv_heads=8, head_dim=64, block_size=16,
