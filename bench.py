@@ -67,8 +67,8 @@ def algorithmic_bytes(b) -> dict:
 
 # the sources the decode kernels and their launcher are built from, and the
 # build script whose compiler flags shape the code too
-DECODE_SOURCES = ("decode.hip", "decode_gqa_mfma.hip", "decode_common.h", "kv_encode.h", "pa_internal.h",
-                  "pa_api.cpp", "../build.py")
+DECODE_SOURCES = ("decode.hip", "decode_gqa_mfma.hip", "decode_gqa16_mfma.hip", "decode_common.h", "kv_encode.h",
+                  "pa_internal.h", "pa_api.cpp", "../build.py")
 
 
 def source_hash() -> str:

@@ -552,7 +552,9 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
             else err = launch_run_t<PA_BF16, PA_FP8_E4M3>(a, head_dim, st);
             if (err != 0) return err;
         }
-        if (plan.geo.mfma) err = launch_decode_gqa_mfma(a, plan, group_size, stream);
+        if (plan.geo.mfma)
+            err = kv_dtype == PA_FP8_E4M3 ? launch_decode_gqa_mfma(a, plan, group_size, stream)
+                                          : launch_decode_gqa16_mfma(a, plan, kv_dtype, group_size, stream);
         else if (kv_dtype == PA_F16) err = launch_t<PA_F16, PA_F16>(a, plan, head_dim, group_size, st);
         else if (kv_dtype == PA_BF16) err = launch_t<PA_BF16, PA_BF16>(a, plan, head_dim, group_size, st);
         else err = launch_t<PA_BF16, PA_FP8_E4M3>(a, plan, head_dim, group_size, st);

@@ -249,7 +249,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
                 const int blk = th < seg_t1 ? __builtin_amdgcn_readlane(my_blk, (th >> shift) - seg0) : -1;
                 half_ok[u] = th < seg_t1 && blk >= 0 && blk < a.num_blocks;
             }
-            // stage the step's K and V rows (row 16u + 8j + lane/8, chunk lane%8)
+            // stage the step's K and V rows (row 16u + 8j + lane/8, chunk
+            // lane%8).  V rows past the end (or of a dropped half) are staged
+            // as zeros: their weight is 0, and 0 times whatever a redirected
+            // load returned (the slot the fused write is storing, a NaN) must
+            // not reach O.  (K rows need no care: their scores are masked.)
+            const bool full = half_ok[0] && half_ok[1] && t0 + kStepTokens <= seg_t1;   // uniform
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -257,6 +262,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
                     const uint32_t off = (uint32_t)((16 * u + 8 * j + (lane >> 3)) * kRowStride + 16 * (lane & 7));
                     *reinterpret_cast<uint4*>(sk + off) = kr[2 * u + j];
                     *reinterpret_cast<uint4*>(sv + off) = vr[2 * u + j];
+                }
+            }
+            if (!full) {      // the masked rows' V, overwritten (one wave's LDS stores land in order)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const uint32_t off = (uint32_t)((16 * u + 8 * j + (lane >> 3)) * kRowStride + 16 * (lane & 7));
+                        if (!(half_ok[u] && t0 + 16 * u + 8 * j + (lane >> 3) < seg_t1))
+                            *reinterpret_cast<uint4*>(sv + off) = make_uint4(0, 0, 0, 0);
+                    }
                 }
             }
             // QK: S[token][head] for both halves; A operand of lane (token n,
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[4 * u + i] = sacc[u][i];
             }
-            if (!(half_ok[0] && half_ok[1] && t0 + kStepTokens <= seg_t1)) {
+            if (!full) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
 #pragma unroll

@@ -32,9 +32,11 @@ constexpr int kMaxPartition = 1 << 20;
 
 DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size, int block_size) {
     DecodeGeometry g;
-    // fp8 KV is only paired with a bf16 query (checked with the arguments);
-    // the matrix-core kernel walks 16-token halves that must not cross a block
-    g.mfma = block_size >= 16 && gqa_mfma_supported(PA_BF16, kv_dtype, head_dim, group_size);
+    // fp8 KV is only paired with a bf16 query, 16-bit KV with a query of its
+    // own dtype (checked with the arguments); the matrix-core kernels walk
+    // 16-token steps that must not cross a block
+    g.mfma = block_size >= 16 && (gqa_mfma_supported(PA_BF16, kv_dtype, head_dim, group_size) ||
+                                  gqa16_mfma_supported(kv_dtype, kv_dtype, head_dim, group_size));
     g.kv_bytes = kv_dtype == PA_FP8_E4M3 ? 1 : 2;
     g.row_lanes = head_dim * g.kv_bytes / 16;
     g.rows = g.mfma ? kDecodeWaves : 64 / g.row_lanes;

@@ -19,11 +19,11 @@ constexpr int kDecodeWaves = kDecodeThreads / 64;
 // 16-byte load each, so one wave-wide load covers `rows` = 64 / row_lanes
 // consecutive KV heads of one token.  A workgroup owns such a group of heads.
 //
-// Grouped-query attention over fp8 KV with head_dim 128 runs instead on the
-// matrix cores (decode_gqa_mfma.hip): one wave per KV head, 4 KV heads per
-// workgroup.
+// Grouped-query attention with head_dim 128 runs instead on the matrix cores
+// (decode_gqa_mfma.hip for fp8 KV, decode_gqa16_mfma.hip for fp16 / bf16
+// KV): one wave per KV head, 4 KV heads per workgroup.
 struct DecodeGeometry {
-    bool mfma;       // grouped-query fp8 kernel on the matrix cores
+    bool mfma;       // grouped-query kernel on the matrix cores
     int kv_bytes;    // bytes per KV element
     int row_lanes;   // lanes per KV-head row (vector kernel)
     int rows;        // KV heads per workgroup
@@ -31,6 +31,7 @@ struct DecodeGeometry {
 };
 
 bool gqa_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int group_size);
+bool gqa16_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int group_size);
 DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size, int block_size);
 
 // Host-side launch plan of one pa_decode call.
@@ -128,6 +129,8 @@ constexpr int kPhaseMerge = 2;
 int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype, pa_dtype kv_dtype,
                   int head_dim, int group_size, int phases, void* stream);
 int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream);
+int launch_decode_gqa16_mfma(const DecodeArgs& a, const DecodePlan& plan, pa_dtype kv_dtype, int group_size,
+                             void* stream);
 int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream);
 int launch_copy_blocks(const CopyArgs& a, void* stream);
 int64_t prefill_grid(int num_seqs, int num_kv_heads, int group_size, int max_new_tokens);

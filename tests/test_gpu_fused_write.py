@@ -23,6 +23,9 @@ CASES = {
     "mha_bf16_d64_bs32": ([5, 32, 33, 64, 257], 8, 8, 64, 32, "bf16", "bf16"),
     "mha_f16_bs8": ([1, 8, 9, 100], 16, 16, 128, 8, "f16", "f16"),
     "gqa4_f16_bs16": ([40, 200, 3], 32, 8, 128, 16, "f16", "f16"),
+    # 16-bit matrix-core kernel; 17, 33, 49: the newest token opens a 16-token step alone
+    "gqa8_bf16_mfma_bs16": ([17, 33, 1, 200, 49], 16, 2, 128, 16, "bf16", "bf16"),
+    "gqa2_f16_mfma_bs32": ([33, 65, 97, 300], 16, 8, 128, 32, "f16", "f16"),
     "gqa4_fp8_mfma_bs16": ([16, 17, 100, 333, 1, 64], 32, 8, 128, 16, "bf16", "fp8_e4m3"),
     "gqa2_fp8_mfma_bs32": ([33, 1, 95, 288], 16, 8, 128, 32, "bf16", "fp8_e4m3"),
     "gqa8_fp8_mfma_partial_group": ([40, 160], 16, 2, 128, 16, "bf16", "fp8_e4m3"),

@@ -81,6 +81,11 @@ SMALL_CASES = {
     "mha_f16_d128_bs8": ([1, 7, 8, 9, 100, 301], 16, 16, 128, 8, "f16", "f16"),
     "gqa2_bf16_d64_bs8": ([3, 50, 77, 130], 8, 4, 64, 8, "bf16", "bf16"),
     "gqa4_fp8_d128_bs8": ([16, 100, 333, 1], 32, 8, 128, 8, "bf16", "fp8_e4m3"),
+    # 16-bit GQA with head_dim 128 on the matrix cores (block 8: the vector kernel)
+    "gqa4_bf16_d128_bs16": ([1, 17, 100, 333, 700], 32, 8, 128, 16, "bf16", "bf16"),
+    "gqa8_f16_d128_bs32": ([5, 33, 64, 257], 16, 2, 128, 32, "f16", "f16"),
+    "gqa8_bf16_d128_partial_wave_group": ([70, 300], 48, 6, 128, 16, "bf16", "bf16"),
+    "gqa4_f16_d128_bs8": ([16, 100, 333], 16, 4, 128, 8, "f16", "f16"),
 }
 
 
@@ -92,7 +97,8 @@ def test_small_case(name):
 
 
 @pytest.mark.parametrize("scale", [-0.0883883476, 0.0])
-@pytest.mark.parametrize("case", ["mha_f16_d128_bs16", "gqa4_fp8_d128_bs16", "gqa8_bf16_d64_partial_group"])
+@pytest.mark.parametrize("case", ["mha_f16_d128_bs16", "gqa4_fp8_d128_bs16", "gqa8_bf16_d64_partial_group",
+                                  "gqa4_bf16_d128_bs16"])
 def test_negative_and_zero_scale(case, scale):
     """Any finite softmax scale: the matrix-core kernel keeps scores unscaled
     and applies the scale in the exponent (a negative scale moved onto the
