@@ -22,6 +22,7 @@ from .configs import (
     make_mixed,
     make_prefix_shared,
     make_gqa_fp8,
+    make_gqa_bf16,
     make_custom,
     CONFIG_MAKERS,
 )
@@ -37,6 +38,7 @@ __all__ = [
     "make_mixed",
     "make_prefix_shared",
     "make_gqa_fp8",
+    "make_gqa_bf16",
     "make_custom",
     "CONFIG_MAKERS",
     "PrefillBatch",

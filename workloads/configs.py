@@ -27,6 +27,10 @@ num_kv_heads, head_dim] from [CANN notes §2.1]):
   gqa_fp8     256 seqs, 32 query heads over 8 KV heads, head_dim 128, bf16
               query, fp8 e4m3 KV with per-tensor fp32 scales, block_size 16,
               lognormal lengths (median 1000, sigma 1, clipped to [16, 8192]).
+  gqa_bf16    64 seqs, 64 query heads over 8 KV heads (GQA-8), head_dim 128,
+              bf16 query and KV, block_size 16, lengths uniform in
+              [512, 4096] (16-bit grouped-query decode, beyond the pages'
+              workloads: the matrix-core kernel for 16-bit KV).
 """
 from __future__ import annotations
 
@@ -284,6 +288,12 @@ def make_gqa_fp8(seed: int = 5, num_seqs: int = 256, max_len: int = 8192) -> Pag
                   max_blocks_per_seq=blocks_for_tokens(max_len, 16))
 
 
+def make_gqa_bf16(seed: int = 6, num_seqs: int = 64, min_len: int = 512, max_len: int = 4096) -> PagedBatch:
+    """GQA-8 with bf16 KV: 64 query heads over 8 KV heads, D 128, bs 16, U[512, 4096] lengths."""
+    return _build("gqa_bf16", seed, lambda rng: rng.integers(min_len, max_len, size=num_seqs, endpoint=True),
+                  64, 8, 128, 16, "bf16", "bf16")
+
+
 def make_custom(name: str, seed: int, lens, num_heads: int, num_kv_heads: int, head_dim: int,
                 block_size: int, q_dtype: str, kv_dtype: str, **kw) -> PagedBatch:
     """Any other shape (scaled-down parity cases, edge cases)."""
@@ -299,4 +309,5 @@ CONFIG_MAKERS = {
     "mixed_bs32": lambda seed=3: make_mixed(seed, 32),
     "prefix13b": make_prefix_shared,
     "gqa_fp8": make_gqa_fp8,
+    "gqa_bf16": make_gqa_bf16,
 }
