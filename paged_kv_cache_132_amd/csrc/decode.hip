@@ -546,8 +546,10 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
     if (plan.grid == 0) return 0;
     int err = 0;
     if (phases & kPhasePartials) {
-        if (a.share_run > 1) {             // the runs' shared partitions first (vector path, one query head per KV head)
-            if (kv_dtype == PA_F16) err = launch_run_t<PA_F16, PA_F16>(a, head_dim, st);
+        if (a.share_run > 1) {             // the runs' shared partitions first (one query head per KV head)
+            if (gqa16_mfma_supported(kv_dtype, kv_dtype, head_dim, a.share_run) && a.block_size >= 16)
+                err = launch_run_gqa16_mfma(a, kv_dtype, stream);
+            else if (kv_dtype == PA_F16) err = launch_run_t<PA_F16, PA_F16>(a, head_dim, st);
             else if (kv_dtype == PA_BF16) err = launch_run_t<PA_BF16, PA_BF16>(a, head_dim, st);
             else err = launch_run_t<PA_BF16, PA_FP8_E4M3>(a, head_dim, st);
             if (err != 0) return err;

@@ -128,9 +128,13 @@ __device__ __forceinline__ float from_lane(float x, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
-template <int KVT, int G, bool WRITE>
+// RUN: the shared-run form (one query head per KV head): query row n of KV
+// head g is head g of sequence s + n, for the G sequences of run s / G, over a
+// partition the run shares (read once, streamed).
+template <int KVT, int G, bool WRITE, bool RUN = false>
 __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(DecodeArgs a) {
     static_assert(G == 2 || G == 4 || G == 8, "query heads per KV head");
+    static_assert(!(RUN && WRITE), "a shared partition never holds a newest token");
     using M = Mma16<KVT>;
     using V8 = typename M::V8;
     constexpr int NW = kDecodeWaves;
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
 
     // ---- which (sequence, KV-head group, partition) -------------------------
     WorkItem w;
-    if (!find_work(a, blockIdx.x, w)) return;
+    if (!(RUN ? find_run_work(a, blockIdx.x, w) : find_work(a, blockIdx.x, w))) return;
     const int s = w.s, p = w.p, group = w.group, L = w.L, n_part = w.n_part;
 
     const int lane = threadIdx.x & 63;
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
     const int Hq = a.num_heads;
     uint16_t* out = static_cast<uint16_t*>(a.out);
 
-    if (L <= 0) {
+    if (!RUN && L <= 0) {
         uint16_t* dst = out + ((int64_t)s * Hq + g * G) * kD;
         for (int i = lane; i < G * kD; i += 64) dst[i] = 0;
         return;
@@ -166,7 +170,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
     const float sscale = fmaxf(fabsf(a.score_scale), 1.17549435e-38f);
     V8 qop[4];
     {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.query) + ((int64_t)s * Hq + g * G + (n < G ? n : 0)) * kD + 8 * q;
+        const int nq = n < G ? n : 0;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.query) +
+                             (RUN ? (int64_t)(s + nq) * Hq + g : (int64_t)s * Hq + g * G + nq) * kD + 8 * q;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             uint4 v = n < G ? *reinterpret_cast<const uint4*>(qp + 32 * c) : make_uint4(0, 0, 0, 0);
@@ -212,7 +218,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
         // shared prefix) go through the caches; the rest are streamed
         const int prev_blk = in_seg && s > 0 ? bt_row[seg0 + lane - a.max_blocks_per_seq] : -1;
         const int next_blk = in_seg && s + 1 < a.num_seqs ? bt_row[seg0 + lane + a.max_blocks_per_seq] : -1;
-        const uint64_t shared = __builtin_amdgcn_ballot_w64(in_seg && (my_blk == prev_blk || my_blk == next_blk));
+        // (the run form reads each block once: streamed)
+        const uint64_t shared = RUN ? 0ull : __builtin_amdgcn_ballot_w64(in_seg && (my_blk == prev_blk || my_blk == next_blk));
         const int seg_t0 = max(t_begin, seg0 << shift);
         const int seg_t1 = min(t_end, (seg0 + seg_blocks) << shift);
         const int n_steps = (seg_t1 - seg_t0 + kStep - 1) / kStep;
@@ -362,16 +369,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float mr = from_lane(m_run, 4 * q + i);
-        const int hl = 4 * q + i;                     // head within the group
+        const int hl = 4 * q + i;                     // head within the group (RUN: sequence within the run)
         if (hl >= G) continue;
-        const int h = g * G + hl;
+        const int h = RUN ? g : g * G + hl;
+        const int so = RUN ? s + hl : s;              // the output's sequence
         if (n_part == 1) {
             const float inv = a.v_scale / lacc[i];
-            uint16_t* dst = out + ((int64_t)s * Hq + h) * kD + n;
+            uint16_t* dst = out + ((int64_t)so * Hq + h) * kD + n;
 #pragma unroll
             for (int t = 0; t < 8; ++t) dst[16 * t] = M::round(oacc[t][i] * inv);
         } else {
-            const int64_t slot = ((int64_t)s * Hq + h) * P + p;
+            const int64_t slot = ((int64_t)so * Hq + h) * P + p;
             float* po = a.part_o + slot * kD + n;
 #pragma unroll
             for (int t = 0; t < 8; ++t) po[16 * t] = oacc[t][i];
@@ -414,6 +422,22 @@ int launch_decode_gqa16_mfma(const DecodeArgs& a, const DecodePlan& plan, pa_dty
             return (int)hipErrorInvalidValue;
     }
     hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+    return (int)hipGetLastError();
+}
+
+int launch_run_gqa16_mfma(const DecodeArgs& a, pa_dtype kv_dtype, void* stream) {
+    const int64_t grid = (int64_t)(a.num_seqs / a.share_run) * a.groups * a.max_partitions;
+    if (grid == 0) return 0;
+    if (grid > INT32_MAX) return (int)hipErrorInvalidValue;
+    const bool f16 = kv_dtype == PA_F16;
+    void (*kernel)(DecodeArgs);
+    switch (a.share_run) {
+        case 2: kernel = f16 ? decode_gqa16_mfma_kernel<PA_F16, 2, false, true> : decode_gqa16_mfma_kernel<PA_BF16, 2, false, true>; break;
+        case 4: kernel = f16 ? decode_gqa16_mfma_kernel<PA_F16, 4, false, true> : decode_gqa16_mfma_kernel<PA_BF16, 4, false, true>; break;
+        case 8: kernel = f16 ? decode_gqa16_mfma_kernel<PA_F16, 8, false, true> : decode_gqa16_mfma_kernel<PA_BF16, 8, false, true>; break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecodeThreads), 0, static_cast<hipStream_t>(stream), a);
     return (int)hipGetLastError();
 }
 

@@ -131,6 +131,8 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
 int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream);
 int launch_decode_gqa16_mfma(const DecodeArgs& a, const DecodePlan& plan, pa_dtype kv_dtype, int group_size,
                              void* stream);
+// the shared-run form on the matrix cores (16-bit KV, head_dim 128, block size >= 16)
+int launch_run_gqa16_mfma(const DecodeArgs& a, pa_dtype kv_dtype, void* stream);
 int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream);
 int launch_copy_blocks(const CopyArgs& a, void* stream);
 int64_t prefill_grid(int num_seqs, int num_kv_heads, int group_size, int max_new_tokens);
