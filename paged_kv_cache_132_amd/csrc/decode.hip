@@ -40,6 +40,11 @@
 // With WRITE (pa_decode_write) the wave that will load a sequence's newest
 // token first stores that token's encoded K/V rows, each lane the bytes it
 // later reads back itself (see the block before the main loop).
+//
+// With RUN (pa_decode_shared, one query head per KV head) the same kernel is
+// the run kernel of shared runs where the matrix-core form does not apply
+// (fp8 KV, head_dim 64, block 8): its G "query heads" are head g of the run's
+// G sequences, over a partition the run shares, each K/V row read once.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>

@@ -34,7 +34,10 @@
 // Output, partials and the merge are shared with the other decode kernels.
 // With WRITE (pa_decode_write) the 16 lanes whose loads will cover a
 // sequence's newest token store its K/V row first, each lane the 16 bytes it
-// later reads itself.
+// later reads itself.  With RUN (pa_decode_shared, one query head per KV
+// head) the query rows are head g of a shared run's sequences and the
+// workgroup covers a partition the run shares: each K/V row is read once for
+// the whole run.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
