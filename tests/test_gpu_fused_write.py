@@ -13,7 +13,7 @@ import oracle
 import paged_kv_cache_132_amd as pa
 from tests._gpu import (assert_decode_close, dev16, dev_i32, dev_pool, gpu_fp8_pool_from_source, host_bits,
                         oracle_decode_sampled, poison_unused, pool_of)
-from workloads import make_custom, make_gqa_fp8, make_llama7b
+from workloads import make_custom, make_gqa_bf16, make_gqa_fp8, make_llama7b
 
 pytestmark = pytest.mark.gpu
 
@@ -181,3 +181,12 @@ def test_gqa_fp8_full_size_bench_step():
     b = make_gqa_fp8()
     lens = b.context_lens
     _check_bench_step(b, gpu_fp8_pool_from_source(b), [int(np.argmin(lens)), int(np.argmax(lens)), 0, 128, 255])
+
+
+def test_gqa_bf16_full_size_bench_step():
+    """GQA-8 over bf16 KV at full size through the bench's own step (16-bit
+    matrix-core kernel, write fused): written slots bit-exact, sampled outputs
+    within 2e-3 plus the output's bf16 half-ulp of the oracle."""
+    b = make_gqa_bf16()
+    lens = b.context_lens
+    _check_bench_step(b, dev_pool(b.kv_pool, "bf16"), [int(np.argmin(lens)), int(np.argmax(lens)), 0, 31, 63])
