@@ -33,6 +33,8 @@ CASES = {
     "bf16_d64_group8_bs32": ([330, 260, 500, 288, 700, 321, 452, 299] * 2, 8, 256, 4, 64, 32, "bf16", "bf16"),
     "fp8_d128_group4": ([200, 300, 150, 400] * 4, 4, 128, 8, 128, 16, "bf16", "fp8_e4m3"),
     "f16_d128_group2_short": ([70, 200, 65, 64, 300, 129, 40, 520], 2, 64, 8, 128, 16, "f16", "f16"),
+    # 16-bit, head_dim 128, block 32: the matrix-core run kernel over two 16-token steps per block
+    "bf16_d128_group4_bs32": ([260, 400, 129, 610, 300, 288, 97, 450], 4, 128, 8, 128, 32, "bf16", "bf16"),
 }
 
 
