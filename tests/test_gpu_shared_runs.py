@@ -126,3 +126,37 @@ def test_prefix13b_full_size_runs_of_8():
     seqs = [0, 7, 9, 30, 63]
     ref = oracle_decode(b, b.kv_pool, b.query, bt, L, seqs=seqs)
     assert_decode_close(got, ref, b, seqs=seqs)
+
+
+def test_shared_runs_graph_replays_match_eager():
+    """The shared-run step (run kernel, per-sequence kernel, merge) captured in a
+    HIP graph: every replay, with eager work and synchronisations between
+    replays, equals the eager call bit for bit."""
+    lens = [300, 420, 257, 700, 512, 390, 301, 640]
+    b = make_custom("shared_graph", 250, lens, 8, 8, 128, 16, "bf16", "bf16", share_group=4,
+                    shared_prefix_tokens=256)
+    bt, L = dev_i32(b.block_table_array()), dev_i32(b.context_lens)
+    pool_dev = dev_pool(pool_of(b), "bf16")
+    q = dev16(b.query, "bf16")
+    ws = pa.Workspace()
+    args = (q, pool_dev, bt, L, b.scale)
+    eager = torch.empty_like(q)
+    pa.decode(*args, out=eager, workspace=ws, partition_size=64, run_size=4)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pa.decode(*args, out=out, workspace=ws, partition_size=64, run_size=4)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        pa.decode(*args, partition_size=64)                # other eager work on the same pool
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+    ref = oracle_decode(b, pool_of(b), b.query, b.block_table_array(), b.context_lens)
+    assert_decode_close(oracle.to_f64(host_bits(out), "bf16"), ref, b)
