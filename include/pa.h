@@ -48,6 +48,9 @@
  * max_blocks_per_seq * block_size -- the results are then meaningless, but
  * memory outside the arguments is never touched.
  *
+ * Size limit: one K (or V) half of a block, block_size * num_kv_heads *
+ * head_dim elements, must stay below 4 GiB (else PA_ERR_BAD_SHAPE).
+ *
  * Supported: head_dim 64 or 128; block_size 8, 16 or 32; num_heads a multiple
  * of num_kv_heads with num_heads / num_kv_heads in {1, 2, 4, 8} (query head h
  * reads KV head h / (num_heads / num_kv_heads)); (query, kv) dtypes
@@ -113,9 +116,16 @@ pa_status pa_cache_write(void* kv_pool, pa_dtype kv_dtype,
                          float k_scale, float v_scale, void* stream);
 
 /*
- * pa_decode_partition_size -- tokens per split-K partition pa_decode will use
- * for these arguments.  `requested` 0 lets the library choose; a positive
- * multiple of block_size is taken as given.  Returns 0 for invalid arguments.
+ * pa_decode_partition_size -- how pa_decode splits sequences for split-K with
+ * these arguments.  A positive `requested` (a multiple of block_size) is a
+ * fixed partition: every sequence is cut into pieces of that many tokens,
+ * and that value is returned.  `requested` 0 leaves the split to the
+ * library: the batch's tokens, laid end to end (each sequence padded to
+ * whole blocks), are cut on the device, per call, into equal chunks, one per
+ * workgroup the GPU holds at once, so every compute unit is dealt the same
+ * number of tokens; a chunk may span several sequences.  The return value is
+ * then the shortest chunk the library uses.  Returns 0 for invalid
+ * arguments.
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size,
@@ -124,8 +134,10 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t nu
 
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs with
- * the same arguments (same `partition_size`).  Returns 0 for invalid
- * arguments.  The workspace holds per-partition partial results.
+ * the same arguments (same `partition_size`) on the current device.  Returns
+ * 0 for invalid arguments.  The workspace holds the partial results of the
+ * split-K pieces and, with partition_size 0, where each sequence's pieces
+ * lie.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size,
@@ -148,18 +160,20 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  *   out           out     [num_seqs, num_heads, head_dim] of q_dtype
  *   query         in      [num_seqs, num_heads, head_dim] of q_dtype
  *   kv_pool       in      [num_blocks, 2, block_size, num_kv_heads, head_dim] of kv_dtype
- *   partition_size        0 = library choice, else a positive multiple of block_size:
- *                         tokens per split-K partition (a sequence shorter than one
- *                         partition is not split)
+ *   partition_size        0 = library choice (equal token chunks across the batch, see
+ *                         pa_decode_partition_size), else a positive multiple of
+ *                         block_size: tokens per split-K partition (a sequence shorter
+ *                         than one partition is not split)
  *   workspace     scratch device memory of at least pa_decode_workspace_size(...) bytes
  *                         for per-partition partial results.  Its contents on entry do not
  *                         matter.  Calls that may run concurrently need separate workspaces.
  *
- * Two kernels on `stream`: workgroups of the first own (sequence, group of KV
- * heads, partition) and write either the final output (single-partition
- * sequences) or a partial softmax state; the second merges the partials of
- * split sequences.  Output does not depend on which physical blocks the
- * table names, only on their logical order.
+ * Two kernels on `stream`: workgroups of the first own a group of KV heads
+ * and a token range (one partition of one sequence, or one chunk of the
+ * batch) and write, for each sequence range they cover, either the final
+ * output (the sequence's whole range) or a partial softmax state; the second
+ * merges the partials of split sequences.  Output does not depend on which
+ * physical blocks the table names, only on their logical order.
  */
 pa_status pa_decode(void* out, const void* query, pa_dtype q_dtype,
                     const void* kv_pool, pa_dtype kv_dtype,

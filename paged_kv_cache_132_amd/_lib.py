@@ -267,14 +267,20 @@ def decode_partition_size(num_seqs: int, num_heads: int, num_kv_heads: int, head
 
 class Workspace:
     """A device workspace for pa_decode, grown on demand (its contents on
-    entry do not matter, so one buffer serves calls of any size on one stream)."""
+    entry do not matter, so one buffer serves calls of any size on one stream).
+
+    A buffer is allocated on the stream the calls that use it launch on:
+    when it grows, the caching allocator hands the old one out again only
+    after the work already queued on that stream."""
 
     def __init__(self):
         self.buf: torch.Tensor | None = None
 
-    def get(self, nbytes: int, device) -> torch.Tensor:
+    def get(self, nbytes: int, device, stream=None) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self.buf = None
+            with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(device)):
+                self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         return self.buf
 
 
@@ -308,10 +314,13 @@ def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tenso
         raise ValueError("out must match query")
     kvt = pa_dtype(kv_pool)
     need = decode_workspace_size(B, hq, hkv, d, bs, mb, kvt, partition_size)
+    launch = torch.cuda.current_stream() if stream is None else stream
     if workspace is None:
-        workspace = _default_ws.setdefault((query.device, torch.cuda.current_stream().cuda_stream), Workspace())
+        # one default workspace per (device, launch stream): calls on different
+        # streams never share partials
+        workspace = _default_ws.setdefault((query.device, launch.cuda_stream), Workspace())
     if isinstance(workspace, Workspace):
-        ws = workspace.get(need, query.device)
+        ws = workspace.get(need, query.device, launch)
     else:
         ws = workspace
     extra = ()

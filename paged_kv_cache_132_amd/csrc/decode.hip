@@ -167,8 +167,6 @@ __device__ __forceinline__ void accumulate_v(float (&o)[EPL], float p, const uin
     }
 }
 
-template <int QT, int D, int NE>
-__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h, int d0, int n_part);
 
 // RUN: the run kernel.  G is then the run length: "query head" gi of KV
 // head g is head g of sequence s + gi (num_heads == num_kv_heads), and the
@@ -190,12 +188,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     __shared__ float s_l[NW][ROWS];
     __shared__ float s_o[NW][64 * EPL];
 
-    // ---- which (sequence, KV-head group, partition) -------------------------
+    // ---- which KV-head group, and which sequences' tokens -------------------
     WorkItem w;
-    if (!(RUN ? find_run_work(a, blockIdx.x, w) : find_work(a, blockIdx.x, w))) return;
-    const int s = w.s, p = w.p, group = w.group, L = w.L, n_part = w.n_part;
+    if (!(RUN ? find_run_work(a, blockIdx.x, w) : begin_work(a, blockIdx.x, w))) return;
+    const int group = w.group;
 
-    const int tid = threadIdx.x;
+    const int Hq = a.num_heads;
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+
+    // one segment (tokens [t0, t1) of one sequence) per pass; every wave of
+    // the workgroup walks the same segments
+    do {
+    // The lane's indices are derived afresh in every pass (from a value the
+    // compiler cannot see through): computed once before the loop they would
+    // stay live through the main loop and cost a wave per SIMD.
+    const int tid = opaque(threadIdx.x);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane / ROWL;
@@ -203,19 +210,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int g_row = group * ROWS + r;
     const bool row_ok = g_row < a.num_kv_heads;
     const int g = row_ok ? g_row : a.num_kv_heads - 1;   // rows past the last head idle on a valid one
-    const int Hq = a.num_heads;
-    uint16_t* out = static_cast<uint16_t*>(a.out);
-
+    const int s = w.s, L = w.L;
+    const int64_t seg_slot = w.seg_slot;
+    // the output is written here, with no merge: the segment is its sequence's whole range
+    const bool whole = RUN ? w.n_part == 1 : whole_sequence(w);
+    if (!RUN) publish_segments(a, w);
     if (!RUN && L <= 0) {                                  // empty sequence: zero output
         if (wave == 0 && row_ok) {
+            const uint32_t z = opaque(0);                  // (a zero made here, not held through the loop)
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) {
                 uint16_t* dst = out + ((int64_t)s * Hq + g * G + gi) * D + j * EPL;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) dst[e] = 0;
+                for (int e = 0; e < EPL; e += 8) *reinterpret_cast<uint4*>(dst + e) = make_uint4(z, z, z, z);
             }
         }
-        return;
+        continue;
     }
 
     // ---- query slices of the G query heads that read KV head g ------------
@@ -235,8 +245,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
 
     // ---- the partition's token range and this lane's K/V addressing -------
-    const int t_begin = p * a.partition;
-    const int t_end = min(L, t_begin + a.partition);
+    const int t_begin = w.t0;
+    const int t_end = w.t1;
     const int shift = a.block_shift;
     const uint32_t row_bytes = (uint32_t)(a.num_kv_heads * D * KVB);        // one token row, all heads
     const uint32_t half_bytes = row_bytes << shift;                       // K half -> V half
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
     const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     // the fused write applies to lengths the table holds (as pa_cache_write)
-    const bool write_len = WRITE && a.context_lens[s] == L;
+    const bool write_len = WRITE && w.L_raw == L;
 
     float m[G], l[G], o[G][EPL];
 #pragma unroll
@@ -387,7 +397,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int mj = ln % ROWL;
     const int mg_row = group * ROWS + mr;
     const bool m_ok = mg_row < a.num_kv_heads;
-    const int P = a.max_partitions;
 
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
@@ -421,13 +430,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         const int so = RUN ? s + gi : s;                  // the output's sequence
         const int d0 = mj * EPL + part * OPT;
         if (m_ok) {
-            if (n_part == 1) {
+            if (whole) {
                 const float inv = a.v_scale / Lsum;
                 uint16_t* dst = out + ((int64_t)so * Hq + h) * D + d0;
 #pragma unroll
                 for (int e = 0; e < OPT; ++e) dst[e] = to_out_bits<QT>(acc[e] * inv);
             } else {
-                const int64_t slot = ((int64_t)so * Hq + h) * P + p;
+                // (a run member's partial: its own sequence's slot of the partition)
+                const int64_t slot = (RUN ? seg_slot + (int64_t)gi * a.max_partitions : seg_slot) * Hq + h;
                 float* po = a.part_o + slot * D + d0;
 #pragma unroll
                 for (int e = 0; e < OPT; ++e) po[e] = acc[e];
@@ -439,33 +449,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         }
         __syncthreads();
     }
+    } while (!RUN && next_segment(a, w));
 }
 
 // Split-K merge of one sequence's partitions for NE consecutive output
 // elements [d0, d0 + NE) of query head h:
 //     M = max_p m_p,  out = v_scale * sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
 template <int QT, int D, int NE>
-__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h, int d0, int n_part) {
-    const int64_t base = ((int64_t)s * a.num_heads + h) * a.max_partitions;
-    const float* ml = a.part_ml + base * 2;
-    const float* po = a.part_o + base * D + d0;
-    // One pass with a running maximum: every partition's loads are
-    // independent of the others, so they are all in flight together.
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h, int d0, const MergeList& list) {
+    // One pass with a running maximum: every partial's loads are independent
+    // of the others, so they are all in flight together.
     float M = -INFINITY;
     float den = 0.f;
     float num[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) num[e] = 0.f;
 #pragma unroll 4
-    for (int pp = 0; pp < n_part; ++pp) {
-        const float mp = ml[pp * 2];
-        const float lp = ml[pp * 2 + 1];
+    for (int i = 0; i < list.n; ++i) {
+        const int64_t slot = list.slot(i) * a.num_heads + h;
+        const float mp = a.part_ml[slot * 2];
+        const float lp = a.part_ml[slot * 2 + 1];
+        const float* po = a.part_o + slot * D + d0;
         const float m_new = fmaxf(M, mp);
-        const float alpha = fast_exp2(M - m_new);      // 0 on the first partition
+        const float alpha = fast_exp2(M - m_new);      // 0 on the first partial
         const float f = fast_exp2(mp - m_new);
         den = fmaf(den, alpha, f * lp);
 #pragma unroll
-        for (int e = 0; e < NE; ++e) num[e] = fmaf(num[e], alpha, f * po[(int64_t)pp * D + e]);
+        for (int e = 0; e < NE; ++e) num[e] = fmaf(num[e], alpha, f * po[e]);
         M = m_new;
     }
     const float inv = a.v_scale / den;
@@ -475,7 +485,7 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
 }
 
 // Second pass of split-K: one thread per output element of every sequence
-// that was split into more than one partition.
+// whose range was split between workgroups.
 template <int QT, int D>
 __global__ __launch_bounds__(kDecodeThreads) void merge_kernel(DecodeArgs a) {
     constexpr int HPB = kDecodeThreads / D;          // query heads per workgroup
@@ -483,18 +493,15 @@ __global__ __launch_bounds__(kDecodeThreads) void merge_kernel(DecodeArgs a) {
     const int s = blockIdx.x / chunks;
     const int h = (blockIdx.x % chunks) * HPB + threadIdx.x / D;
     const int d = threadIdx.x % D;
-    const int max_tokens = a.max_blocks_per_seq << a.block_shift;
-    const int L = min(a.context_lens[s], max_tokens);
-    const int n_part = L > 0 ? (L + a.partition - 1) / a.partition : 0;
-    if (n_part <= 1 || h >= a.num_heads) return;
-    merge_partials<QT, D, 1>(a, s, h, d, n_part);
+    const MergeList list = merge_list(a, s);
+    if (list.n <= 1 || h >= a.num_heads) return;
+    merge_partials<QT, D, 1>(a, s, h, d, list);
 }
 
 template <int QT, int KVT, int D>
-int launch_d(const DecodeArgs& a, const DecodePlan& plan, int group_size, hipStream_t st) {
-    const dim3 grid((unsigned)plan.grid), block(kDecodeThreads);
+int launch_d(const DecodeArgs& args, const DecodePlan& plan, int group_size, hipStream_t st) {
     void (*kernel)(DecodeArgs);
-    const bool w = a.new_key != nullptr;
+    const bool w = args.new_key != nullptr;
     switch (group_size) {
         case 1: kernel = w ? decode_kernel<QT, KVT, D, 1, true> : decode_kernel<QT, KVT, D, 1, false>; break;
         case 2: kernel = w ? decode_kernel<QT, KVT, D, 2, true> : decode_kernel<QT, KVT, D, 2, false>; break;
@@ -502,7 +509,10 @@ int launch_d(const DecodeArgs& a, const DecodePlan& plan, int group_size, hipStr
         case 8: kernel = w ? decode_kernel<QT, KVT, D, 8, true> : decode_kernel<QT, KVT, D, 8, false>; break;
         default: return (int)hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+    DecodeArgs a = args;
+    const int64_t grid = decode_grid(&a, plan, reinterpret_cast<const void*>(kernel), 0);
+    if (grid <= 0 || grid > INT32_MAX) return grid == 0 ? 0 : (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecodeThreads), 0, st, a);
     return (int)hipGetLastError();
 }
 
@@ -566,7 +576,10 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
         else if (kv_dtype == PA_BF16) err = launch_t<PA_BF16, PA_BF16>(a, plan, head_dim, group_size, st);
         else err = launch_t<PA_BF16, PA_FP8_E4M3>(a, plan, head_dim, group_size, st);
     }
-    if (err != 0 || !(phases & kPhaseMerge) || plan.max_partitions <= 1) return err;
+    // no merge when no sequence can be split: one fixed partition holds every
+    // table, or a single chunk the whole batch
+    const bool can_split = a.partition > 0 ? plan.max_partitions > 1 : plan.max_chunks > 1;
+    if (err != 0 || !(phases & kPhaseMerge) || !can_split) return err;
     const bool f16 = q_dtype == PA_F16;
     if (head_dim == 64) return f16 ? launch_merge<PA_F16, 64>(a, st) : launch_merge<PA_BF16, 64>(a, st);
     return f16 ? launch_merge<PA_F16, 128>(a, st) : launch_merge<PA_BF16, 128>(a, st);

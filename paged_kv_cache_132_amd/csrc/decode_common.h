@@ -1,4 +1,6 @@
-// Device helpers shared by the two decode kernels.
+// Device helpers shared by the decode kernels: which tokens of which
+// sequences a workgroup attends over, where its partial results go, and how
+// the merge finds them again.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,12 +11,46 @@
 
 namespace pa {
 
-// One decode work item: partition p of sequence s for KV-head group `group`.
+// One segment of a workgroup's work: tokens [t0, t1) of sequence s, for the
+// KV heads of group `group`.
+//
+// Fixed partitions (a.partition > 0): a workgroup owns partition p of one
+// sequence (one segment).  Token chunks (a.partition == 0): a workgroup owns
+// chunk c of the batch's tokens laid end to end, and walks the one or more
+// sequences the chunk covers, one segment each.
 struct WorkItem {
     int s, p, group;
-    int L;        // context length, cut to the table's capacity
-    int n_part;   // partitions of sequence s (0 for an empty sequence)
+    int L;          // context length, cut to the table's capacity
+    int L_raw;      // context_lens[s] as given
+    int n_part;     // fixed partitions: partitions of sequence s (0 for an empty sequence)
+    int t0, t1;     // the segment's tokens [t0, t1)
+    // token chunks: the chunk, the chunk count and the batch's padded length
+    // in blocks, the chunk's padded token range [pos, end), and sequence s's
+    // padded offset
+    int chunk, n_chunks, units, pos, end, off;
+    int64_t seg_slot;   // partial-result slot of this segment (times num_heads, plus the head)
 };
+
+constexpr int kCachedChunks = 8;                  // sequences 0..511 keep their length in registers
+constexpr int kXcds = 8;                          // accelerator complex dies of the chip
+
+// Items a sequence of length L is cut into with item length T; an empty
+// sequence still has one item, which writes its zero output.
+__device__ __forceinline__ int items_for(int L, int T) { return L > 0 ? (L + T - 1) / T : 1; }
+
+// Tokens a sequence occupies in the chunk layout: its length rounded up to
+// whole blocks, so every chunk boundary falls on a block boundary of the
+// sequence it cuts; an empty sequence takes one block (its zero output).
+__device__ __forceinline__ int padded_len(int L, int block_size) {
+    return L > 0 ? (L + block_size - 1) & ~(block_size - 1) : block_size;
+}
+
+// x, through an empty asm statement: values computed from the result are
+// computed where they are used, not hoisted out of a loop around them.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
@@ -34,21 +70,21 @@ __device__ __forceinline__ int wave_total(int v) {
 // Whether the batch shares prefix blocks between neighbouring sequences, as
 // prefix caching and parallel sampling produce: some probe pair of
 // neighbours (four pairs spread over the batch) maps its first logical block
-// to the same physical block.  A handful of scalar loads; every wave gets
-// the same answer.
+// to the same physical block.  Lanes 0..3 load one pair each, all at once;
+// every wave gets the same answer.
 __device__ inline bool batch_shares_prefix(const DecodeArgs& a) {
     const int B = a.num_seqs;
     if (B < 2) return false;
-    bool shared = false;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int s = k * (B - 2) / 3;                     // 0 .. B - 2
-        if (a.context_lens[s] > 0 && a.context_lens[s + 1] > 0) {
-            const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-            shared |= bt[0] == bt[a.max_blocks_per_seq];
-        }
+    const int lane = threadIdx.x & 63;
+    bool pair = false;
+    if (lane < 4) {
+        const int s = lane * (B - 2) / 3;                  // 0 .. B - 2
+        const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+        const int l0 = a.context_lens[s], l1 = a.context_lens[s + 1];
+        const int b0 = bt[0], b1 = bt[a.max_blocks_per_seq];
+        pair = l0 > 0 && l1 > 0 && b0 == b1;
     }
-    return shared;
+    return __builtin_amdgcn_ballot_w64(pair) != 0;
 }
 
 // Whether run k (sequences R*k .. R*k + R - 1, R = a.share_run) shares
@@ -78,7 +114,135 @@ __device__ inline bool run_shares_partition(const DecodeArgs& a, int k, int p) {
     return __builtin_amdgcn_ballot_w64(!ok) == 0;
 }
 
-// Map workgroup `wg` to the wg-th live work item.
+// Lengths of sequences lane + 64 i, i < kCachedChunks (0 past the batch):
+// one load per lane and chunk of 64, all issued together.
+__device__ __forceinline__ void load_lengths(const DecodeArgs& a, int (&len_raw)[kCachedChunks]) {
+    const int lane = threadIdx.x & 63;
+    const int chunks = (a.num_seqs + 63) >> 6;                 // uniform
+#pragma unroll
+    for (int i = 0; i < kCachedChunks; ++i) {
+        const int s = lane + 64 * i;
+        len_raw[i] = (i < chunks && s < a.num_seqs) ? a.context_lens[s] : 0;
+    }
+}
+
+// Value of v held by lane (s & 63) of register (s >> 6), s < 512 and uniform.
+// (Each register is read out on its own and the results selected, so that
+// the array is never indexed by a variable and stays in registers.)
+__device__ __forceinline__ int cached_at(const int (&v)[kCachedChunks], int s) {
+    int x = 0;
+#pragma unroll
+    for (int i = 0; i < kCachedChunks; ++i) {
+        const int vi = __builtin_amdgcn_readlane(v[i], s & 63);
+        x = (s >> 6) == i ? vi : x;
+    }
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Token chunks (partition 0, the library's choice).
+//
+// The sequences' tokens are laid end to end, each sequence padded to whole
+// blocks (`units` blocks in all), and cut at block boundaries into N chunks
+// of near-equal length: chunk c holds blocks [c*units/N, (c+1)*units/N).  N
+// is the number of workgroup slots the GPU holds at once divided among the
+// KV-head groups, so that every workgroup starts in the first dispatch round
+// and every compute unit is dealt about the same number of tokens -- a
+// compute unit streams at about a fixed rate, so it is the tokens per unit,
+// not per workgroup, that decide when the last one finishes.  Chunks are not
+// shorter than part_min tokens, so small batches take fewer of them.  A
+// chunk covers the end of one sequence, whole sequences, and the start of
+// another, each a segment; a segment that is not its sequence's whole range
+// leaves a partial result for the merge, in slot 2c (the chunk's first
+// segment) or 2c + 1 (its last), which no other segment of the chunk can
+// need.
+
+// first padded token of chunk c
+__device__ __forceinline__ int chunk_start(int c, int n_chunks, int units, int block_size) {
+    return (int)((int64_t)c * units / n_chunks) * block_size;
+}
+
+// chunk holding padded token x
+__device__ __forceinline__ int chunk_of(int x, int n_chunks, int units, int block_size) {
+    return (int)(((int64_t)(x / block_size + 1) * n_chunks - 1) / units);
+}
+
+__device__ inline bool begin_chunk_work(const DecodeArgs& a, int wg, WorkItem& w) {
+    const int lane = threadIdx.x & 63;
+    const int B = a.num_seqs;
+    const int U = a.block_size;
+    const int max_tokens = a.max_blocks_per_seq << a.block_shift;
+    int len_raw[kCachedChunks], padded[kCachedChunks];
+    load_lengths(a, len_raw);
+#pragma unroll
+    for (int i = 0; i < kCachedChunks; ++i)
+        padded[i] = lane + 64 * i < B ? padded_len(min(len_raw[i], max_tokens), U) : 0;
+    // padded tokens of sequences [0, s): every wave computes the same sums
+    auto offset_of = [&](int s) {
+        int acc = 0;
+#pragma unroll
+        for (int i = 0; i < kCachedChunks; ++i) acc += lane + 64 * i < s ? padded[i] : 0;
+        for (int x = lane + 64 * kCachedChunks; x < s; x += 64)
+            acc += padded_len(min(a.context_lens[x], max_tokens), U);
+        return wave_total(acc);
+    };
+    const int total = offset_of(B);
+    const int units = total / U;
+    const int slots = max(a.target_items / a.groups, 1);
+    const int n = max(1, min(min(slots, (total + a.part_min - 1) / a.part_min), units));
+    const int items = n * a.groups;
+    if (wg >= items) return false;
+    // The hardware deals workgroup ids round-robin to the XCDs (id % kXcds);
+    // renumber so that each XCD takes a contiguous run of chunks: the
+    // KV-head groups of one chunk, and neighbouring sequences (which may
+    // share prefix blocks), then share that XCD's L2.
+    const int x = wg % kXcds, j = wg / kXcds;
+    const int per = items / kXcds, rem = items % kXcds;
+    const int item = x * per + min(x, rem) + j;
+    w.chunk = item / a.groups;
+    w.group = item % a.groups;
+    w.n_chunks = n;
+    w.units = units;
+    w.pos = chunk_start(w.chunk, n, units, U);
+    w.end = chunk_start(w.chunk + 1, n, units, U);
+    // the sequence holding the chunk's first token: the last s with
+    // offset(s) <= pos (offsets grow strictly: every sequence takes a block)
+    int lo = 0, hi = B;                                           // offset(lo) <= pos < offset(hi)
+    int off_lo = 0;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        const int off_mid = offset_of(mid);
+        if (off_mid <= w.pos) { lo = mid; off_lo = off_mid; }
+        else hi = mid;
+    }
+    w.s = lo;
+    w.off = off_lo;
+    w.L_raw = lo < 64 * kCachedChunks ? cached_at(len_raw, lo) : a.context_lens[lo];
+    w.L = min(w.L_raw, max_tokens);
+    w.p = 0;
+    w.n_part = 0;
+    w.t0 = w.pos - w.off;
+    w.t1 = min(w.L, w.end - w.off);
+    w.seg_slot = 2 * (int64_t)w.chunk;
+    return true;
+}
+
+// The next sequence of the chunk, if the chunk reaches it.  Its length is
+// loaded here, together with whatever the segment loads next.
+__device__ inline bool next_chunk_segment(const DecodeArgs& a, WorkItem& w) {
+    w.off += padded_len(w.L, a.block_size);
+    ++w.s;
+    if (w.off >= w.end || w.s >= a.num_seqs) return false;
+    w.L_raw = a.context_lens[w.s];
+    w.L = min(w.L_raw, a.max_blocks_per_seq << a.block_shift);
+    w.t0 = 0;
+    w.t1 = min(w.L, w.end - w.off);
+    w.seg_slot = 2 * (int64_t)w.chunk + 1;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed partitions.
 //
 // Items are (sequence s, partition p < items(s), KV-head group) with
 // items(s) = max(n_part(s), 1) (an empty sequence has one item, which writes
@@ -100,25 +264,20 @@ __device__ inline bool run_shares_partition(const DecodeArgs& a, int k, int p) {
 // a partition p, and the item's sequence is one of them, in order.
 // Each wave computes this on its own -- no LDS, no barriers -- so waves of a
 // workgroup may call it independently; they all reach the same answer.
-constexpr int kXcds = 8;                          // accelerator complex dies of the chip
-
-__device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
-    constexpr int kCached = 8;                    // sequences 0..511 keep their count in registers
+__device__ inline bool begin_partition_work(const DecodeArgs& a, int wg, WorkItem& w) {
+    constexpr int kCached = kCachedChunks;
     const int lane = threadIdx.x & 63;
     const int B = a.num_seqs;
     const int P = a.max_partitions;
+    const int T = a.partition;
     const int max_tokens = a.max_blocks_per_seq << a.block_shift;
-    auto items_of = [&](int s) {
-        const int L = min(a.context_lens[s], max_tokens);
-        return L > 0 ? (L + a.partition - 1) / a.partition : 1;
-    };
+    const bool shares = batch_shares_prefix(a);                   // its loads go out with the lengths'
+    int len_raw[kCached];
+    load_lengths(a, len_raw);
     int cached[kCached];
 #pragma unroll
-    for (int i = 0; i < kCached; ++i) {
-        const int s = lane + 64 * i;
-        cached[i] = s < B ? items_of(s) : 0;
-    }
-    auto items_at = [&](int i, int s) { return i < kCached ? cached[i] : (s < B ? items_of(s) : 0); };
+    for (int i = 0; i < kCached; ++i) cached[i] = lane + 64 * i < B ? items_for(min(len_raw[i], max_tokens), T) : 0;
+    auto items_of = [&](int s) { return items_for(min(a.context_lens[s], max_tokens), T); };
     auto C = [&](int p) {
         int acc = 0;
 #pragma unroll
@@ -126,10 +285,8 @@ __device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
         for (int s = lane + 64 * kCached; s < B; s += 64) acc += min(items_of(s), p);
         return wave_total(acc);
     };
-    // Live items are workgroups 0 .. total-1.  The hardware deals workgroup
-    // ids round-robin to the XCDs (id % kXcds); renumber so that each XCD
-    // takes a contiguous run of items: the KV-head groups of one (sequence,
-    // partition) and neighbouring sequences then share that XCD's L2.
+    // Live items are workgroups 0 .. total-1, renumbered per XCD as in the
+    // chunk layout
     const int total = C(P) * a.groups;
     if (wg >= total) return false;                // past the last item
     const int x = wg % kXcds, j = wg / kXcds;
@@ -148,7 +305,7 @@ __device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
     const int p = lo;
     const int c_p = C(p);
     int rank, group;                              // rank: among sequences with items(s) > p, ascending s
-    if (batch_shares_prefix(a)) {
+    if (shares) {
         const int n_p = C(p + 1) - c_p;           // >= 1: the item lies in partition p
         const int local = item - c_p * a.groups;
         group = local / n_p;
@@ -157,30 +314,98 @@ __device__ inline bool find_work(const DecodeArgs& a, int wg, WorkItem& w) {
         group = item % a.groups;
         rank = k - c_p;
     }
+    // the rank-th sequence (ascending) with more than p items: count them 64
+    // at a time (registers first, then loads past 512)
     int s_found = -1;
-    for (int c0 = 0, i = 0; c0 < B; c0 += 64, ++i) {
-        const int s = c0 + lane;
-        const uint64_t bits = __builtin_amdgcn_ballot_w64(s < B && items_at(i, s) > p);
+    auto pick = [&](int c0, bool has_item) {
+        const uint64_t bits = __builtin_amdgcn_ballot_w64(has_item);
         const int cnt = __builtin_popcountll(bits);
-        if (rank < cnt) {
+        if (s_found < 0 && rank < cnt) {
             // lane whose bit is set with exactly `rank` set bits below it
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
             const uint64_t hit = __builtin_amdgcn_ballot_w64(((bits >> lane) & 1ull) && (int)below == rank);
             s_found = c0 + (int)__builtin_ctzll(hit);
-            break;
         }
         rank -= cnt;
-    }
+    };
+#pragma unroll
+    for (int i = 0; i < kCached; ++i)
+        if (s_found < 0 && 64 * i < B) pick(64 * i, cached[i] > p);
+    for (int c0 = 64 * kCached; s_found < 0 && c0 < B; c0 += 64) pick(c0, c0 + lane < B && items_of(c0 + lane) > p);
     if (s_found < 0) return false;
     w.s = s_found;
     w.p = p;
     w.group = group;
-    w.L = min(a.context_lens[s_found], max_tokens);
-    w.n_part = w.L > 0 ? (w.L + a.partition - 1) / a.partition : 0;
+    w.L_raw = s_found < 64 * kCached ? cached_at(len_raw, s_found) : a.context_lens[s_found];
+    w.L = min(w.L_raw, max_tokens);
+    w.n_part = w.L > 0 ? (w.L + T - 1) / T : 0;
+    w.t0 = p * T;
+    w.t1 = min(w.L, w.t0 + T);
+    w.chunk = -1;
+    w.seg_slot = (int64_t)s_found * P + p;
     // a partition a shared run holds is the run kernel's
     if (a.share_run > 1 && run_shares_partition(a, s_found / a.share_run, p)) return false;
     return true;
+}
+
+// The first segment of workgroup `wg` of a per-sequence decode kernel.
+__device__ __forceinline__ bool begin_work(const DecodeArgs& a, int wg, WorkItem& w) {
+    return a.partition > 0 ? begin_partition_work(a, wg, w) : begin_chunk_work(a, wg, w);
+}
+
+// Advance to the workgroup's next segment; false when it has none.
+__device__ __forceinline__ bool next_segment(const DecodeArgs& a, WorkItem& w) {
+    return a.partition > 0 ? false : next_chunk_segment(a, w);
+}
+
+// Whether the segment is its sequence's whole range (the output is written
+// directly, no partial).
+__device__ __forceinline__ bool whole_sequence(const WorkItem& w) { return w.t0 == 0 && w.t1 >= w.L; }
+
+// Token chunks: the workgroup of group 0 that holds a sequence's first token
+// records where the sequence's partials lie -- chunk of the first one, its
+// slot within that chunk, how many -- for the merge.  Thread 0, once per
+// sequence and call.
+__device__ __forceinline__ void publish_segments(const DecodeArgs& a, const WorkItem& w) {
+    if (a.partition > 0 || w.group != 0 || w.t0 != 0 || threadIdx.x != 0) return;
+    int32_t* h = a.part_n + 4 * (int64_t)w.s;
+    const int first = w.chunk;
+    const int last = w.L > 0 ? chunk_of(w.off + w.L - 1, w.n_chunks, w.units, a.block_size) : first;
+    h[0] = w.L > 0 ? last - first + 1 : 0;
+    h[1] = first;
+    h[2] = (int)(w.seg_slot - 2 * (int64_t)w.chunk);               // 0: starts the chunk, 1: does not
+}
+
+// Partials of sequence s for the merge: their count (0 or 1: no merge), and
+// slot(i) of the i-th, in token order.
+struct MergeList {
+    int n;
+    int64_t base;       // fixed partitions: s * P; token chunks: 2 * first chunk + its slot
+    bool chunked;
+    __device__ __forceinline__ int64_t slot(int i) const {
+        return chunked ? (i == 0 ? base : (base & ~1ll) + 2 * (int64_t)i) : base + i;
+    }
+};
+
+__device__ __forceinline__ MergeList merge_list(const DecodeArgs& a, int s) {
+    MergeList m;
+    const int L = min(a.context_lens[s], a.max_blocks_per_seq << a.block_shift);
+    m.chunked = a.partition == 0;
+    if (L <= 0) {
+        m.n = 0;
+        m.base = 0;
+    } else if (!m.chunked) {
+        m.n = (L + a.partition - 1) / a.partition;
+        m.base = (int64_t)s * a.max_partitions;
+    } else {
+        // as the attention pass recorded it, kept within the workspace
+        const int32_t* h = a.part_n + 4 * (int64_t)s;
+        const int first = min(max(h[1], 0), a.max_chunks - 1);
+        m.n = min(max(h[0], 0), a.max_chunks - first);
+        m.base = 2 * (int64_t)first + (h[2] & 1);
+    }
+    return m;
 }
 
 // Map workgroup `wg` of the run kernel to (run k, KV-head group, partition p):
@@ -195,8 +420,13 @@ __device__ inline bool find_run_work(const DecodeArgs& a, int wg, WorkItem& w) {
     w.s = k * a.share_run;
     w.p = p;
     w.group = group;
-    w.L = min(a.context_lens[w.s], a.max_blocks_per_seq << a.block_shift);
+    w.L_raw = a.context_lens[w.s];
+    w.L = min(w.L_raw, a.max_blocks_per_seq << a.block_shift);
     w.n_part = (w.L + a.partition - 1) / a.partition;
+    w.t0 = p * a.partition;
+    w.t1 = min(w.L, w.t0 + a.partition);
+    w.chunk = -1;
+    w.seg_slot = (int64_t)w.s * a.max_partitions + p;    // run member i: (s + i) * max_partitions + p
     return true;
 }
 

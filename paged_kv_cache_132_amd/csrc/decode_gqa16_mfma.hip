@@ -19,9 +19,9 @@
 //         head_dim positions; zero for n >= G).  4 MFMAs give S[token][head],
 //         lane (q, n) holding tokens 4q .. 4q + 3 of head n.
 //   soft  running max over the step (in-lane, then across the 4 lane rows by
-//         permlane swaps), exp2-domain probabilities rounded once to the MFMA
-//         type; the reference max moves only when a head's max grows by more
-//         than 2^8.
+//         permlane swaps), exp2-domain probabilities rounded to the MFMA type
+//         (bf16: plus a rounded remainder, see PV); the reference max moves
+//         only when a head's max grows by more than 2^8.
 //   PV    v_mfma_f32_16x16x16_{f16,bf16}: A = P, exactly the lane's own 4
 //         probabilities (k-slot 4q + j is token 4q + j); B = V read from its
 //         row-major LDS copy with ds_read_b64_tr_b16 -- within a 16-lane group
@@ -29,7 +29,12 @@
 //         4j + i / 4, so lane 4j + m addresses V[4q + j][16t + 4m] and lane i
 //         receives column 16t + i of tokens 4q .. 4q + 3.  8 MFMAs (16
 //         head_dim columns each) accumulate O[head][d] in fp32, and one more,
-//         P times a column of ones, the running sums.
+//         P times a column of ones, the running sums.  With bf16 KV the
+//         probabilities are split into a bf16 part and a bf16 remainder and
+//         both go through PV and the sums: one bf16 rounding (2^-9 relative)
+//         would move an output of a peaked softmax by up to 2^-9 times the
+//         spread of the V rows it weights, while the pair carries about 16
+//         significant bits.  fp16 (2^-11) keeps a single rounding.
 //
 // Output, partials and the merge are shared with the other decode kernels.
 // With WRITE (pa_decode_write) the 16 lanes whose loads will cover a
@@ -84,6 +89,7 @@ struct Mma16<PA_F16> {
     }
     static __device__ __forceinline__ uint16_t round(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
     static constexpr uint32_t kOne2 = 0x3C003C00u;      // two 1.0 values
+    static constexpr bool kSplit = false;               // P rounded once (2^-11 relative)
 };
 
 template <>
@@ -105,6 +111,10 @@ struct Mma16<PA_BF16> {
         return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
     }
     static constexpr uint32_t kOne2 = 0x3F803F80u;
+    static constexpr bool kSplit = true;                // P = bf16 part + bf16 remainder
+    // the two values of a packed pair, widened exactly
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -146,22 +156,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
 
     // ---- which (sequence, KV-head group, partition) -------------------------
     WorkItem w;
-    if (!(RUN ? find_run_work(a, blockIdx.x, w) : find_work(a, blockIdx.x, w))) return;
-    const int s = w.s, p = w.p, group = w.group, L = w.L, n_part = w.n_part;
-
-    const int lane = threadIdx.x & 63;
+    if (!(RUN ? find_run_work(a, blockIdx.x, w) : begin_work(a, blockIdx.x, w))) return;
+    const int group = w.group;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = group * NW + wave;                 // this wave's KV head
     if (g >= a.num_kv_heads) return;                 // no barriers below: idle waves may leave
-    const int n = lane & 15;
-    const int q = lane >> 4;
     const int Hq = a.num_heads;
     uint16_t* out = static_cast<uint16_t*>(a.out);
 
+    // one segment (tokens [t0, t1) of one sequence) per pass
+    do {
+    if (!RUN) publish_segments(a, w);                // (thread 0: wave 0 always holds a KV head)
+    const int lane = opaque(threadIdx.x) & 63;       // (derived in every pass, see decode.hip)
+    const int n = lane & 15;
+    const int q = lane >> 4;
+    const int s = w.s, L = w.L;
+    const int64_t seg_slot = w.seg_slot;
+    const bool whole = RUN ? w.n_part == 1 : whole_sequence(w);
+
     if (!RUN && L <= 0) {
         uint16_t* dst = out + ((int64_t)s * Hq + g * G) * kD;
-        for (int i = lane; i < G * kD; i += 64) dst[i] = 0;
-        return;
+        const uint32_t z = opaque(0);
+        for (int i = lane * 8; i < G * kD; i += 64 * 8) *reinterpret_cast<uint4*>(dst + i) = make_uint4(z, z, z, z);
+        continue;
     }
 
     // ---- query operand: head n of this KV head's group, head_dim 32c + 8q ----
@@ -187,8 +204,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
         }
     }
 
-    const int t_begin = p * a.partition;
-    const int t_end = min(L, t_begin + a.partition);
+    const int t_begin = w.t0;
+    const int t_end = w.t1;
     const int shift = a.block_shift;
     const uint32_t row_bytes = (uint32_t)(a.num_kv_heads * kD * 2);          // one token row, all heads
     const uint32_t half_bytes = row_bytes << shift;                           // K half -> V half
@@ -196,7 +213,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
     const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     // the fused write applies to lengths the table holds (as pa_cache_write)
-    const bool write_len = WRITE && a.context_lens[s] == L;
+    const bool write_len = WRITE && w.L_raw == L;
 
     uint16_t* sk = s_k[wave];
     uint16_t* sv = s_v[wave];
@@ -328,21 +345,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
 #pragma unroll
                 for (int i = 0; i < 4; ++i) lacc[i] *= ar[i];
             }
-            // probabilities rounded once (RNE, in pairs): the same values feed
-            // the PV product and the running sum
-            const uint2 pop = make_uint2(M::round2(fast_exp2(fmaf(sc[0], sscale, -m_sub)),
-                                                   fast_exp2(fmaf(sc[1], sscale, -m_sub))),
-                                         M::round2(fast_exp2(fmaf(sc[2], sscale, -m_sub)),
-                                                   fast_exp2(fmaf(sc[3], sscale, -m_sub))));
-            // PV, and the row sums
+            // probabilities rounded (RNE, in pairs): the same values feed the
+            // PV product and the running sum.  bf16: the remainder p - hi is
+            // exact in fp32 and rounded once more.
+            float pf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pf[i] = fast_exp2(fmaf(sc[i], sscale, -m_sub));
+            const uint2 pop = make_uint2(M::round2(pf[0], pf[1]), M::round2(pf[2], pf[3]));
+            uint2 pop_lo = make_uint2(0u, 0u);
+            if constexpr (M::kSplit)
+                pop_lo = make_uint2(M::round2(pf[0] - M::lo(pop.x), pf[1] - M::hi(pop.x)),
+                                    M::round2(pf[2] - M::lo(pop.y), pf[3] - M::hi(pop.y)));
+            // PV, and the row sums (split: the 8 remainder products after the
+            // 8 leading ones, so no MFMA waits on the one before it)
             __builtin_amdgcn_s_setprio(1);
+            uint2 vop[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(sv + tr_off + 16 * t));
-                oacc[t] = M::pv(pop, __builtin_bit_cast(uint2, v4), oacc[t]);
+                vop[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(sv + tr_off + 16 * t)));
+                oacc[t] = M::pv(pop, vop[t], oacc[t]);
             }
             lacc = M::pv(pop, ones, lacc);
+            if constexpr (M::kSplit) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) oacc[t] = M::pv(pop_lo, vop[t], oacc[t]);
+                lacc = M::pv(pop_lo, ones, lacc);
+            }
             __builtin_amdgcn_s_setprio(0);
         };
 
@@ -368,7 +397,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
     }
 
     // ---- finish: the output or a split-K partial ---------------------------
-    const int P = a.max_partitions;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float mr = from_lane(m_run, 4 * q + i);
@@ -376,13 +404,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
         if (hl >= G) continue;
         const int h = RUN ? g : g * G + hl;
         const int so = RUN ? s + hl : s;              // the output's sequence
-        if (n_part == 1) {
+        if (whole) {
             const float inv = a.v_scale / lacc[i];
             uint16_t* dst = out + ((int64_t)so * Hq + h) * kD + n;
 #pragma unroll
             for (int t = 0; t < 8; ++t) dst[16 * t] = M::round(oacc[t][i] * inv);
         } else {
-            const int64_t slot = ((int64_t)so * Hq + h) * P + p;
+            // (a run member's partial: its own sequence's slot of the partition)
+            const int64_t slot = (RUN ? seg_slot + (int64_t)hl * a.max_partitions : seg_slot) * Hq + h;
             float* po = a.part_o + slot * kD + n;
 #pragma unroll
             for (int t = 0; t < 8; ++t) po[16 * t] = oacc[t][i];
@@ -392,6 +421,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa16_mfma_kernel(Decod
             }
         }
     }
+    } while (!RUN && next_segment(a, w));
 }
 
 }  // namespace
@@ -401,12 +431,11 @@ bool gqa16_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int
            (group_size == 2 || group_size == 4 || group_size == 8);
 }
 
-int launch_decode_gqa16_mfma(const DecodeArgs& a, const DecodePlan& plan, pa_dtype kv_dtype, int group_size,
+int launch_decode_gqa16_mfma(const DecodeArgs& args, const DecodePlan& plan, pa_dtype kv_dtype, int group_size,
                              void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)plan.grid), block(kDecodeThreads);
     void (*kernel)(DecodeArgs);
-    const bool w = a.new_key != nullptr;
+    const bool w = args.new_key != nullptr;
     const bool f16 = kv_dtype == PA_F16;
     switch (group_size) {
         case 2:
@@ -424,7 +453,10 @@ int launch_decode_gqa16_mfma(const DecodeArgs& a, const DecodePlan& plan, pa_dty
         default:
             return (int)hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, a);
+    DecodeArgs a = args;
+    const int64_t grid = decode_grid(&a, plan, reinterpret_cast<const void*>(kernel), 0);
+    if (grid <= 0 || grid > INT32_MAX) return grid == 0 ? 0 : (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecodeThreads), 0, st, a);
     return (int)hipGetLastError();
 }
 

@@ -108,22 +108,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
 
     // ---- which (sequence, KV-head group, partition) -------------------------
     WorkItem w;
-    if (!find_work(a, blockIdx.x, w)) return;
-    const int s = w.s, p = w.p, group = w.group, L = w.L, n_part = w.n_part;
-
-    const int lane = threadIdx.x & 63;
+    if (!begin_work(a, blockIdx.x, w)) return;
+    const int group = w.group;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = group * NW + wave;                 // this wave's KV head
     if (g >= a.num_kv_heads) return;                 // no barriers below: idle waves may leave
-    const int n = lane & 15;
-    const int q = lane >> 4;
     const int Hq = a.num_heads;
     uint16_t* out = static_cast<uint16_t*>(a.out);
 
+    // one segment (tokens [t0, t1) of one sequence) per pass
+    do {
+    publish_segments(a, w);                          // (thread 0: wave 0 always holds a KV head)
+    const int lane = opaque(threadIdx.x) & 63;       // (derived in every pass, see decode.hip)
+    const int n = lane & 15;
+    const int q = lane >> 4;
+    const int s = w.s, L = w.L;
+    const int64_t seg_slot = w.seg_slot;
+    const bool whole = whole_sequence(w);
+
     if (L <= 0) {
         uint16_t* dst = out + ((int64_t)s * Hq + g * G) * kD;
-        for (int i = lane; i < G * kD; i += 64) dst[i] = 0;
-        return;
+        const uint32_t z = opaque(0);
+        for (int i = lane * 8; i < G * kD; i += 64 * 8) *reinterpret_cast<uint4*>(dst + i) = make_uint4(z, z, z, z);
+        continue;
     }
 
     // ---- query operand: head n of this KV head's group, head_dim 32q.. ----
@@ -148,8 +155,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
         }
     }
 
-    const int t_begin = p * a.partition;
-    const int t_end = min(L, t_begin + a.partition);
+    const int t_begin = w.t0;
+    const int t_end = w.t1;
     const int shift = a.block_shift;
     const uint32_t row_bytes = (uint32_t)(a.num_kv_heads * kD);               // fp8: 1 byte per element
     const uint32_t half_bytes = row_bytes << shift;                           // K half -> V half
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     const uint8_t* pool = static_cast<const uint8_t*>(a.kv_pool);
     const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     // the fused write applies to lengths the table holds (as pa_cache_write)
-    const bool write_len = WRITE && a.context_lens[s] == L;
+    const bool write_len = WRITE && w.L_raw == L;
 
     // LDS: this wave's K and V staging rows; transposed-read base address of this lane
     uint8_t* sk = s_kv[wave][0];
@@ -372,7 +379,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
     }
 
     // ---- finish: per-head sums, then the output or a split-K partial -------
-    const int P = a.max_partitions;
     float lr[4], mr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -384,13 +390,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
         const int hl = 4 * q + i;                     // head within the group
         if (hl >= G) continue;
         const int h = g * G + hl;
-        if (n_part == 1) {
+        if (whole) {
             const float inv = a.v_scale / lr[i];
             uint16_t* dst = out + ((int64_t)s * Hq + h) * kD + n;
 #pragma unroll
             for (int t = 0; t < 8; ++t) dst[16 * t] = bf16_bits(oacc[t][i] * inv);
         } else {
-            const int64_t slot = ((int64_t)s * Hq + h) * P + p;
+            const int64_t slot = seg_slot * Hq + h;
             float* po = a.part_o + slot * kD + n;
 #pragma unroll
             for (int t = 0; t < 8; ++t) po[16 * t] = oacc[t][i];
@@ -400,6 +406,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_gqa_fp8_mfma_kernel(Dec
             }
         }
     }
+    } while (next_segment(a, w));
 }
 
 }  // namespace
@@ -409,11 +416,10 @@ bool gqa_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int g
            (group_size == 2 || group_size == 4 || group_size == 8);
 }
 
-int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int group_size, void* stream) {
+int launch_decode_gqa_mfma(const DecodeArgs& args, const DecodePlan& plan, int group_size, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)plan.grid), block(kDecodeThreads);
     void (*kernel)(DecodeArgs);
-    const bool w = a.new_key != nullptr;
+    const bool w = args.new_key != nullptr;
     switch (group_size) {
         case 2: kernel = w ? decode_gqa_fp8_mfma_kernel<2, true> : decode_gqa_fp8_mfma_kernel<2, false>; break;
         case 4: kernel = w ? decode_gqa_fp8_mfma_kernel<4, true> : decode_gqa_fp8_mfma_kernel<4, false>; break;
@@ -428,7 +434,10 @@ int launch_decode_gqa_mfma(const DecodeArgs& a, const DecodePlan& plan, int grou
     constexpr size_t kCapLds = 18432;
     static_assert(3 * (kStaticLds + kCapLds) > 160 * 1024 && 2 * (kStaticLds + kCapLds) <= 160 * 1024,
                   "two workgroups of LDS per CU, not three");
-    hipLaunchKernelGGL(kernel, grid, block, kCapLds, st, a);
+    DecodeArgs a = args;
+    const int64_t grid = decode_grid(&a, plan, reinterpret_cast<const void*>(kernel), kCapLds);
+    if (grid <= 0 || grid > INT32_MAX) return grid == 0 ? 0 : (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecodeThreads), kCapLds, st, a);
     return (int)hipGetLastError();
 }
 

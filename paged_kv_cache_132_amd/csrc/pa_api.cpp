@@ -6,6 +6,12 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <unordered_map>
+
 #include "pa.h"
 #include "pa_internal.h"
 
@@ -67,6 +73,9 @@ pa_status check_decode_args(const void* out, const void* query, pa_dtype q_dtype
     if (partition_size != 0 && (partition_size % block_size != 0 || partition_size > kMaxPartition))
         return PA_ERR_BAD_SHAPE;
     if ((int64_t)max_blocks_per_seq * block_size > (int64_t)INT32_MAX / 2) return PA_ERR_BAD_SHAPE;
+    // the kernels step from a block's K half to its V half with a 32-bit offset
+    if ((int64_t)block_size * num_kv_heads * head_dim * elem_bytes(kv_dtype) > (int64_t)UINT32_MAX)
+        return PA_ERR_BAD_SHAPE;
     if (!isfinite(scale)) return PA_ERR_BAD_SHAPE;
     if (kv_dtype == PA_FP8_E4M3 &&
         !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
@@ -93,28 +102,113 @@ bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
     p.geo = decode_geometry(head_dim, kv_dtype, num_heads / num_kv_heads, block_size);
     p.groups = (num_kv_heads + p.geo.rows - 1) / p.geo.rows;
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
-    int part = partition_size;
-    if (part == 0) {
-        // The largest partition (fewest partials, least per-workgroup start-up)
-        // that still gives at least 2048 workgroups -- 256 CUs several times
-        // over -- when every sequence is at its longest.
+    // The partition the shared-run form takes when the caller leaves it to
+    // the library: the largest (fewest partials, least per-workgroup
+    // start-up) that still gives at least 2048 workgroups -- 256 CUs several
+    // times over -- when every sequence is at its longest.
+    {
         const int64_t heads_x_seqs = (int64_t)p.groups * num_seqs;
-        part = 1024;
+        int part = 1024;
         while (part > 64 && heads_x_seqs * ((max_tokens + part - 1) / part) < 2048) part /= 2;
         if (part < block_size) part = block_size;
-        part = (part + block_size - 1) / block_size * block_size;
+        p.run_partition = (part + block_size - 1) / block_size * block_size;
     }
-    p.partition = part;
-    p.max_partitions = (int)((max_tokens + part - 1) / part);
-    p.grid = (int64_t)p.groups * num_seqs * p.max_partitions;
-    if (p.grid > INT32_MAX) return false;
-    const size_t n_part = (size_t)num_seqs * num_heads * p.max_partitions;
-    p.off_ml = 0;
+    // token chunks: at least 64 tokens (whole blocks) each, and never more
+    // chunks than the GPU holds workgroups at once
+    p.part_min = (64 + block_size - 1) / block_size * block_size;
+    p.max_chunks = std::max(1, slot_cap() / p.groups);
+    int64_t slots;                                   // partial-result slots the workspace holds
+    if (partition_size > 0) {
+        p.partition = partition_size;
+        p.max_partitions = (int)((max_tokens + partition_size - 1) / partition_size);
+        p.grid = (int64_t)p.groups * num_seqs * p.max_partitions;
+        slots = (int64_t)num_seqs * p.max_partitions;
+    } else {
+        p.partition = 0;
+        p.max_partitions = (int)((max_tokens + p.run_partition - 1) / p.run_partition);
+        p.grid = (int64_t)p.groups * p.max_chunks;
+        // room for the chunks' partials, or for the shared-run form's
+        slots = std::max<int64_t>(2 * (int64_t)p.max_chunks, (int64_t)num_seqs * p.max_partitions);
+    }
+    if (p.grid > INT32_MAX || (int64_t)p.groups * num_seqs * p.max_partitions > INT32_MAX) return false;
+    const size_t n_part = (size_t)slots * num_heads;
+    p.off_n = 0;
+    p.off_ml = align_up((size_t)num_seqs * 4 * sizeof(int32_t), 256);
     p.off_o = p.off_ml + align_up(n_part * 2 * sizeof(float), 256);
     p.bytes = p.off_o + align_up(n_part * (size_t)head_dim * sizeof(float), 256);
     if (p.bytes == 0) p.bytes = 256;
     *plan = p;
     return true;
+}
+
+namespace {
+
+struct DeviceCache {
+    std::mutex mu;
+    std::unordered_map<int, int> cus;                                     // device -> compute units
+    std::map<std::tuple<int, const void*, size_t>, int> resident;        // (device, kernel, lds) -> workgroups
+};
+
+DeviceCache& device_cache() {
+    static DeviceCache c;
+    return c;
+}
+
+int current_cus(int* dev_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    *dev_out = dev;
+    DeviceCache& c = device_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    auto it = c.cus.find(dev);
+    if (it != c.cus.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        cus = 0;
+    }
+    c.cus[dev] = cus;
+    return cus;
+}
+
+}  // namespace
+
+int slot_cap() {
+    int dev = 0;
+    const int cus = current_cus(&dev);
+    return cus > 0 ? 8 * cus : 2048;
+}
+
+int resident_workgroups(const void* kernel, size_t dyn_lds) {
+    int dev = 0;
+    const int cus = current_cus(&dev);
+    if (cus <= 0) return 0;
+    DeviceCache& c = device_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    const auto key = std::make_tuple(dev, kernel, dyn_lds);
+    auto it = c.resident.find(key);
+    if (it != c.resident.end()) return it->second;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecodeThreads, dyn_lds) != hipSuccess) {
+        (void)hipGetLastError();
+        per_cu = 0;
+    }
+    const int n = std::min(std::max(per_cu, 0) * cus, 8 * cus);
+    c.resident[key] = n;
+    return n;
+}
+
+int64_t decode_grid(DecodeArgs* a, const DecodePlan& plan, const void* kernel, size_t dyn_lds) {
+    if (a->partition > 0) return plan.grid;
+    // token chunks: one per resident workgroup slot (split among the groups)
+    int slots = resident_workgroups(kernel, dyn_lds);
+    if (slots <= 0) slots = plan.max_chunks * plan.groups;
+    slots = std::min(slots, plan.max_chunks * plan.groups);
+    a->target_items = slots;
+    return (int64_t)std::max(slots / plan.groups, 1) * plan.groups;
 }
 
 }  // namespace pa
@@ -216,7 +310,7 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t nu
     if (!plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      kv_dtype, requested, &p))
         return 0;
-    return p.partition;
+    return requested > 0 ? p.partition : p.part_min;
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -424,6 +518,7 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     char* ws = static_cast<char*>(workspace);
+    a.part_n = reinterpret_cast<int32_t*>(ws + plan.off_n);
     a.part_ml = reinterpret_cast<float*>(ws + plan.off_ml);
     a.part_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.num_seqs = num_seqs;
@@ -436,6 +531,9 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
     a.groups = plan.groups;
     a.partition = plan.partition;
     a.max_partitions = plan.max_partitions;
+    a.part_min = plan.part_min;
+    a.max_chunks = plan.max_chunks;
+    a.target_items = plan.max_chunks * plan.groups;    // the launcher sets it from the kernel's occupancy
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;
     a.new_key = new_key;
@@ -444,6 +542,12 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
     a.write_v_scale = v_scale;
     // shared runs go to the vector kernel's run form: one query head per KV head
     a.share_run = (run_size > 1 && !plan.geo.mfma && num_heads == num_kv_heads) ? run_size : 0;
+    if (a.share_run > 1 && plan.partition == 0) {
+        // the run form walks fixed partitions (the workspace has room for them)
+        plan.partition = plan.run_partition;
+        plan.grid = (int64_t)plan.groups * num_seqs * plan.max_partitions;
+        a.partition = plan.partition;
+    }
     const int err = launch_decode(a, plan, q_dtype, kv_dtype, head_dim, num_heads / num_kv_heads,
                                   phases, stream);
     return err == 0 ? PA_OK : PA_ERR_HIP;

@@ -35,13 +35,23 @@ bool gqa16_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int
 DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size, int block_size);
 
 // Host-side launch plan of one pa_decode call.
+//
+// Fixed partitions (partition > 0): every sequence is cut into pieces of
+// `partition` tokens; a workgroup owns one piece of one sequence.  Token
+// chunks (partition == 0, the library's choice): the batch's tokens, laid end
+// to end, are cut on the device into as many equal chunks as the GPU holds
+// workgroups at once (at least part_min tokens each); a workgroup owns one
+// chunk, which may span several sequences.
 struct DecodePlan {
     DecodeGeometry geo;
     int groups;          // ceil(num_kv_heads / rows)
-    int partition;       // tokens per split-K partition (multiple of block_size)
-    int max_partitions;  // ceil(max_blocks_per_seq * block_size / partition)
-    int64_t grid;        // workgroups launched
-    size_t off_ml, off_o, bytes;   // workspace layout
+    int partition;       // tokens per split-K partition (multiple of block_size); 0: token chunks
+    int part_min;        // token chunks: shortest chunk
+    int max_partitions;  // fixed partitions: ceil(max tokens / partition)
+    int max_chunks;      // token chunks: most chunks a launch can have
+    int run_partition;   // partition the shared-run form uses when the caller leaves it to the library
+    int64_t grid;        // workgroups launched (token chunks: an upper bound, refined at launch)
+    size_t off_n, off_ml, off_o, bytes;   // workspace layout
 };
 
 // Pure argument checks (no HIP calls): shared by the API and the CPU tests.
@@ -62,11 +72,18 @@ struct DecodeArgs {
     const void* kv_pool;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    float* part_ml;         // [num_seqs, num_heads, max_partitions, 2] (max, sum) log2 domain
-    float* part_o;          // [num_seqs, num_heads, max_partitions, head_dim]
+    // Split-K partial results, one slot per segment that is not its
+    // sequence's whole range: fixed partitions, slot s * max_partitions + p;
+    // token chunks, slot 2c or 2c + 1 of chunk c.
+    int32_t* part_n;        // token chunks: [num_seqs, 4] where each sequence's partials lie
+    float* part_ml;         // [slots, num_heads, 2] (max, sum) in the log2 domain
+    float* part_o;          // [slots, num_heads, head_dim]
     int32_t num_seqs, num_heads, num_kv_heads;
     int32_t block_size, block_shift, max_blocks_per_seq, num_blocks;
     int32_t groups, partition, max_partitions;
+    // token chunks (partition == 0): shortest chunk, most chunks, and the
+    // workgroups the attention kernel keeps resident on the whole GPU
+    int32_t part_min, max_chunks, target_items;
     float score_scale;      // scale * k_scale * log2(e): scores in the exp2 domain
     float v_scale;
     // Fused cache write (null: none): the newest token's K/V rows
@@ -121,6 +138,18 @@ struct CopyArgs {
     int64_t num_pairs, block_bytes;
     int32_t src_num_blocks, dst_num_blocks;
 };
+
+// Workgroups of kDecodeThreads threads (and `dyn_lds` bytes of dynamic LDS)
+// of `kernel` the current device holds at once: compute units x resident
+// workgroups per unit, at most slot_cap().  Cached per (device, kernel).
+int resident_workgroups(const void* kernel, size_t dyn_lds);
+// Most workgroups of kDecodeThreads threads any kernel can keep resident on
+// the current device (8 per compute unit); 2048 when the device cannot be
+// asked.
+int slot_cap();
+// Workgroups a decode launch needs for the plan; with token chunks it also
+// sets a->target_items for `kernel`.
+int64_t decode_grid(DecodeArgs* a, const DecodePlan& plan, const void* kernel, size_t dyn_lds);
 
 // Launchers (defined next to their kernels).  Return the hipError_t as int.
 // phase bit 1: attention pass (partials), bit 2: split-K merge.

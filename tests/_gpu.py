@@ -65,6 +65,8 @@ def poison_unused(pool_raw: np.ndarray, tables, lens, kv_dtype: str) -> np.ndarr
 def pool_of(batch) -> np.ndarray:
     """Raw pool the decode reads: 16-bit bits, or oracle-encoded e4m3 codes."""
     if batch.kv_dtype == "fp8_e4m3":
+        if batch.src_dtype == "bf16":
+            return oracle_fp8_pool(batch)
         return oracle.encode_pool(batch.kv_source, batch.src_dtype, "fp8_e4m3", batch.k_scale, batch.v_scale)
     return batch.kv_pool
 
@@ -111,16 +113,18 @@ def gpu_fp8_pool_from_source(batch) -> torch.Tensor:
     return pool
 
 
-def oracle_decode_sampled(batch, pool_raw, query_raw, bt, lens, seqs):
-    """Oracle output rows for a few sequences, encoding (fp8) or copying only
-    the blocks those sequences read."""
-    out = np.zeros((batch.num_seqs, batch.num_heads, batch.head_dim))
-    for s in seqs:
-        blocks = sorted(set(int(x) for x in batch.tables[s]))
-        remap = {blk: i for i, blk in enumerate(blocks)}
-        sub = pool_raw(blocks)
-        bt_s = np.array([[remap[int(x)] for x in batch.tables[s]]], dtype=np.int32)
-        out[s] = oracle.paged_decode(query_raw[s:s + 1], batch.q_dtype, sub, batch.kv_dtype, bt_s,
-                                     lens[s:s + 1], batch.block_size, batch.scale, batch.k_scale,
-                                     batch.v_scale)[0]
-    return out
+def oracle_fp8_pool(batch) -> np.ndarray:
+    """The whole fp8 pool as the oracle encodes it, built fast: the oracle's
+    cache-write encoding is applied once to each of the 65536 bf16 bit
+    patterns (with k_scale for the K half, v_scale for the V half) and the
+    pool's source values are looked up in those two tables.  Exact: the code
+    of a value depends on that value and the scale alone."""
+    assert batch.src_dtype == "bf16" and batch.kv_dtype == "fp8_e4m3"
+    every = np.arange(1 << 16, dtype=np.uint16)
+    k_codes = oracle.encode_for_cache(every, "bf16", "fp8_e4m3", batch.k_scale)
+    v_codes = oracle.encode_for_cache(every, "bf16", "fp8_e4m3", batch.v_scale)
+    pool = np.empty(batch.kv_source.shape, dtype=np.uint8)
+    pool[:, 0] = k_codes[batch.kv_source[:, 0]]
+    pool[:, 1] = v_codes[batch.kv_source[:, 1]]
+    return pool
+

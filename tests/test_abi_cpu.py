@@ -90,6 +90,10 @@ def call_decode(lib, **kw):
     (dict(max_blocks_per_seq=0), SHAPE),
     (dict(num_blocks=0), SHAPE),
     (dict(partition_size=24), SHAPE),
+    # one K (or V) half of a block of 4 GiB or more
+    (dict(num_heads=1 << 20, num_kv_heads=1 << 20, head_dim=128, block_size=16), SHAPE),
+    (dict(q_dtype=BF16, kv_dtype=FP8, num_heads=1 << 21, num_kv_heads=1 << 21, head_dim=128,
+          block_size=16), SHAPE),
     (dict(partition_size=-16), SHAPE),
     (dict(scale=float("inf")), SHAPE),
     (dict(q_dtype=BF16, kv_dtype=FP8, k_scale=0.0), SHAPE),
@@ -165,13 +169,21 @@ def test_write_zero_sequences_is_a_noop(lib):
 
 
 def test_workspace_and_partition_plan(lib):
-    # 7B shape: 32 seqs, 32/32 heads, D 128, bs 16, up to 2048 tokens
+    # 7B shape: 32 seqs, 32/32 heads, D 128, bs 16, up to 2048 tokens.
+    # Token chunks (partition 0): at least 64 tokens each; room for two
+    # partials per chunk, at most 8 resident workgroups per compute unit of
+    # the device (2048 without one), split among the 8 groups of 4 KV heads
     pt = pa.decode_partition_size(32, 32, 32, 128, 16, 128, F16)
-    assert pt % 16 == 0 and 64 <= pt <= 1024
+    assert pt == 64
     ws = pa.decode_workspace_size(32, 32, 32, 128, 16, 128, F16)
-    P = -(-128 * 16 // pt)
-    need = 32 * 32 * P * 2 * 4 + 32 * 32 * P * 128 * 4
-    assert need <= ws <= need + 2 * 256
+    slots = 2 * (2048 // 8)
+    need = 32 * 4 * 4 + slots * 32 * 2 * 4 + slots * 32 * 128 * 4
+    assert need <= ws <= need + 3 * 256
+    # a fixed partition: one slot per (sequence, partition)
+    P = -(-128 * 16 // 256)
+    ws = pa.decode_workspace_size(32, 32, 32, 128, 16, 128, F16, 256)
+    need = 32 * 4 * 4 + 32 * P * 32 * 2 * 4 + 32 * P * 32 * 128 * 4
+    assert need <= ws <= need + 3 * 256
     # explicit partition sizes are honoured; one partition spans the whole table
     assert pa.decode_partition_size(32, 32, 32, 128, 16, 128, F16, 2048) == 2048
     assert pa.decode_partition_size(32, 32, 32, 128, 16, 128, F16, 24) == 0

@@ -114,18 +114,20 @@ def test_write_partials_shared_equals_separate_write():
 
 def test_prefix13b_full_size_runs_of_8():
     """The 13B batch (groups of 8 sharing 140 blocks) with runs of 8 at the
-    default partition: sampled sequences against the oracle, every output
-    within tolerance of the per-sequence decode."""
+    default partition, at 512 tokens and at 640 (the shared prefix is exactly
+    7 partitions): every sequence against the oracle, and within tolerance of
+    the per-sequence decode."""
     b = make_prefix_shared()
     bt, L = b.block_table_array(), b.context_lens
     pool_dev = dev_pool(b.kv_pool, "f16")
-    got = _decode(b, pool_dev, bt, L, 8, 0)
     plain = _decode(b, pool_dev, bt, L, 1, 0)
-    assert np.isfinite(got).all()
-    assert np.abs(got - plain).max() <= 2e-3
-    seqs = [0, 7, 9, 30, 63]
-    ref = oracle_decode(b, b.kv_pool, b.query, bt, L, seqs=seqs)
-    assert_decode_close(got, ref, b, seqs=seqs)
+    ref = oracle_decode(b, b.kv_pool, b.query, bt, L)
+    assert_decode_close(plain, ref, b)
+    for ps in (0, 512, 640):
+        got = _decode(b, pool_dev, bt, L, 8, ps)
+        assert np.isfinite(got).all()
+        assert np.abs(got - plain).max() <= 2e-3, ps
+        assert_decode_close(got, ref, b)
 
 
 def test_shared_runs_graph_replays_match_eager():

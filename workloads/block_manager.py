@@ -19,6 +19,8 @@ is not fixed by the pages; outputs must not depend on it.
 """
 from __future__ import annotations
 
+from collections import deque
+
 import numpy as np
 
 
@@ -44,26 +46,28 @@ class BlockManager:
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
         order = rng.permutation(self.num_blocks) if rng is not None else np.arange(self.num_blocks)
-        self.free_list: list[int] = [int(b) for b in order]
+        # free blocks in the order they are handed out; freed blocks queue at the back
+        self._free: deque[int] = deque(int(b) for b in order)
         self.ref_count = np.zeros(self.num_blocks, dtype=np.int64)
 
     # -- allocation ---------------------------------------------------------
     @property
     def num_free(self) -> int:
-        return len(self.free_list)
+        return len(self._free)
 
     def allocate(self, n: int) -> list[int]:
+        """Take n blocks from the head of the free queue, each with one reference."""
         n = int(n)
         if n < 0:
             raise ValueError("cannot allocate a negative number of blocks")
-        if n > len(self.free_list):
+        if n > len(self._free):
             raise PoolExhausted("KV cache block pool exhausted")
-        blocks = self.free_list[:n]
-        del self.free_list[:n]
-        for b in blocks:
-            assert self.ref_count[b] == 0
-            self.ref_count[b] = 1
-        return blocks
+        taken = [self._free.popleft() for _ in range(n)]
+        ids = np.asarray(taken, dtype=np.int64)
+        if np.any(self.ref_count[ids] != 0):
+            raise AssertionError("a block on the free queue still has references")
+        self.ref_count[ids] = 1
+        return taken
 
     def share(self, blocks: list[int]) -> list[int]:
         """Attach already-allocated blocks to one more table (refcount + 1)."""
@@ -80,7 +84,7 @@ class BlockManager:
                 raise ValueError(f"double free of block {b}")
             self.ref_count[b] -= 1
             if self.ref_count[b] == 0:
-                self.free_list.append(int(b))
+                self._free.append(int(b))
 
     # -- sequence helpers ---------------------------------------------------
     def allocate_for_prompt(self, prompt_len: int) -> list[int]:
