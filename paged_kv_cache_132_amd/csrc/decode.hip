@@ -457,26 +457,36 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 //     M = max_p m_p,  out = v_scale * sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
 template <int QT, int D, int NE>
 __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h, int d0, const MergeList& list) {
-    // One pass with a running maximum: every partial's loads are independent
-    // of the others, so they are all in flight together.
+    // A running maximum over batches of 8 partials: each batch's loads are
+    // all issued before the first is used, so most sequences take one round
+    // trip to memory.
+    constexpr int kBatch = 8;
     float M = -INFINITY;
     float den = 0.f;
     float num[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) num[e] = 0.f;
-#pragma unroll 4
-    for (int i = 0; i < list.n; ++i) {
-        const int64_t slot = list.slot(i) * a.num_heads + h;
-        const float mp = a.part_ml[slot * 2];
-        const float lp = a.part_ml[slot * 2 + 1];
-        const float* po = a.part_o + slot * D + d0;
-        const float m_new = fmaxf(M, mp);
-        const float alpha = fast_exp2(M - m_new);      // 0 on the first partial
-        const float f = fast_exp2(mp - m_new);
-        den = fmaf(den, alpha, f * lp);
+    for (int i0 = 0; i0 < list.n; i0 += kBatch) {
+        float mp[kBatch], lp[kBatch], op[kBatch][NE];
 #pragma unroll
-        for (int e = 0; e < NE; ++e) num[e] = fmaf(num[e], alpha, f * po[e]);
-        M = m_new;
+        for (int k = 0; k < kBatch; ++k) {
+            const int64_t slot = list.slot(min(i0 + k, list.n - 1)) * a.num_heads + h;
+            mp[k] = a.part_ml[slot * 2];
+            lp[k] = a.part_ml[slot * 2 + 1];
+#pragma unroll
+            for (int e = 0; e < NE; ++e) op[k][e] = a.part_o[slot * D + d0 + e];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (i0 + k >= list.n) break;                // uniform: one sequence per workgroup
+            const float m_new = fmaxf(M, mp[k]);
+            const float alpha = fast_exp2(M - m_new);   // 0 on the first partial
+            const float f = fast_exp2(mp[k] - m_new);
+            den = fmaf(den, alpha, f * lp[k]);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) num[e] = fmaf(num[e], alpha, f * op[k][e]);
+            M = m_new;
+        }
     }
     const float inv = a.v_scale / den;
     uint16_t* dst = static_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + h) * D + d0;

@@ -11,6 +11,37 @@
 
 namespace pa {
 
+constexpr int kXcds = 8;                          // accelerator complex dies of the chip
+
+// Where the chunks lie.  Chunk c's work items (one per KV-head group) go to
+// the XCD that the renumbering below gives item c * groups; an XCD with an
+// odd index gets chunks odd_xcd_weight/16 as long as an even one's (the odd
+// XCDs of this part stream measurably slower, whichever tokens they get).
+// Chunk boundaries are whole blocks: chunk c starts at block
+// floor(units * W(c) / W(n)), W(c) the weight of chunks 0 .. c-1.
+struct ChunkLayout {
+    int n, units, groups, per, rem, block_size, w_odd;
+
+    // first chunk whose first item the renumbering gives XCD x (x = 0 .. 8)
+    __device__ __forceinline__ int first_chunk(int x) const {
+        const int64_t i = (int64_t)x * per + min(x, rem);
+        return (int)((i + groups - 1) / groups);
+    }
+    __device__ __forceinline__ int64_t weight_before(int c) const {
+        int64_t W = 0;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int f0 = first_chunk(x), f1 = first_chunk(x + 1);
+            W += (int64_t)((x & 1) ? w_odd : 16) * max(0, min(c, f1) - f0);
+        }
+        return W;
+    }
+    // first padded token of chunk c (c = 0 .. n)
+    __device__ __forceinline__ int start(int c) const {
+        return (int)((int64_t)units * weight_before(c) / weight_before(n)) * block_size;
+    }
+};
+
 // One segment of a workgroup's work: tokens [t0, t1) of sequence s, for the
 // KV heads of group `group`.
 //
@@ -24,15 +55,19 @@ struct WorkItem {
     int L_raw;      // context_lens[s] as given
     int n_part;     // fixed partitions: partitions of sequence s (0 for an empty sequence)
     int t0, t1;     // the segment's tokens [t0, t1)
-    // token chunks: the chunk, the chunk count and the batch's padded length
-    // in blocks, the chunk's padded token range [pos, end), and sequence s's
-    // padded offset
-    int chunk, n_chunks, units, pos, end, off;
+    // token chunks: the chunk, the chunk's padded token range [pos, end),
+    // and sequence s's padded offset
+    int chunk, pos, end, off;
     int64_t seg_slot;   // partial-result slot of this segment (times num_heads, plus the head)
 };
 
+// The chunk layout of a launch with n chunks over `units` blocks.
+__device__ __forceinline__ ChunkLayout chunk_layout(const DecodeArgs& a, int n, int units) {
+    const int items = n * a.groups;
+    return ChunkLayout{n, units, a.groups, items / kXcds, items % kXcds, a.block_size, a.odd_xcd_weight};
+}
+
 constexpr int kCachedChunks = 8;                  // sequences 0..511 keep their length in registers
-constexpr int kXcds = 8;                          // accelerator complex dies of the chip
 
 // Items a sequence of length L is cut into with item length T; an empty
 // sequence still has one item, which writes its zero output.
@@ -157,16 +192,6 @@ __device__ __forceinline__ int cached_at(const int (&v)[kCachedChunks], int s) {
 // segment) or 2c + 1 (its last), which no other segment of the chunk can
 // need.
 
-// first padded token of chunk c
-__device__ __forceinline__ int chunk_start(int c, int n_chunks, int units, int block_size) {
-    return (int)((int64_t)c * units / n_chunks) * block_size;
-}
-
-// chunk holding padded token x
-__device__ __forceinline__ int chunk_of(int x, int n_chunks, int units, int block_size) {
-    return (int)(((int64_t)(x / block_size + 1) * n_chunks - 1) / units);
-}
-
 __device__ inline bool begin_chunk_work(const DecodeArgs& a, int wg, WorkItem& w) {
     const int lane = threadIdx.x & 63;
     const int B = a.num_seqs;
@@ -201,10 +226,10 @@ __device__ inline bool begin_chunk_work(const DecodeArgs& a, int wg, WorkItem& w
     const int item = x * per + min(x, rem) + j;
     w.chunk = item / a.groups;
     w.group = item % a.groups;
-    w.n_chunks = n;
-    w.units = units;
-    w.pos = chunk_start(w.chunk, n, units, U);
-    w.end = chunk_start(w.chunk + 1, n, units, U);
+    const ChunkLayout layout = chunk_layout(a, n, units);
+    w.pos = layout.start(w.chunk);
+    w.end = layout.start(w.chunk + 1);
+    if (w.end <= w.pos) return false;                             // a chunk the weights left empty
     // the sequence holding the chunk's first token: the last s with
     // offset(s) <= pos (offsets grow strictly: every sequence takes a block)
     int lo = 0, hi = B;                                           // offset(lo) <= pos < offset(hi)
@@ -363,18 +388,19 @@ __device__ __forceinline__ bool next_segment(const DecodeArgs& a, WorkItem& w) {
 // directly, no partial).
 __device__ __forceinline__ bool whole_sequence(const WorkItem& w) { return w.t0 == 0 && w.t1 >= w.L; }
 
-// Token chunks: the workgroup of group 0 that holds a sequence's first token
-// records where the sequence's partials lie -- chunk of the first one, its
-// slot within that chunk, how many -- for the merge.  Thread 0, once per
+// Token chunks: where each sequence's partials lie, for the merge.  The
+// workgroup of group 0 that holds a sequence's first token records that
+// chunk and the slot its segment took there (0: it starts the chunk); the
+// one that holds its last token records that chunk.  Thread 0, once per
 // sequence and call.
 __device__ __forceinline__ void publish_segments(const DecodeArgs& a, const WorkItem& w) {
-    if (a.partition > 0 || w.group != 0 || w.t0 != 0 || threadIdx.x != 0) return;
+    if (a.partition > 0 || w.group != 0 || threadIdx.x != 0) return;
     int32_t* h = a.part_n + 4 * (int64_t)w.s;
-    const int first = w.chunk;
-    const int last = w.L > 0 ? chunk_of(w.off + w.L - 1, w.n_chunks, w.units, a.block_size) : first;
-    h[0] = w.L > 0 ? last - first + 1 : 0;
-    h[1] = first;
-    h[2] = (int)(w.seg_slot - 2 * (int64_t)w.chunk);               // 0: starts the chunk, 1: does not
+    if (w.t0 == 0) {
+        h[1] = w.chunk;
+        h[2] = (int)(w.seg_slot - 2 * (int64_t)w.chunk);
+    }
+    if (w.t1 >= w.L) h[0] = w.chunk;
 }
 
 // Partials of sequence s for the merge: their count (0 or 1: no merge), and
@@ -390,8 +416,11 @@ struct MergeList {
 
 __device__ __forceinline__ MergeList merge_list(const DecodeArgs& a, int s) {
     MergeList m;
-    const int L = min(a.context_lens[s], a.max_blocks_per_seq << a.block_shift);
     m.chunked = a.partition == 0;
+    // the length and (token chunks) the record of the attention pass, loaded together
+    const int L = min(a.context_lens[s], a.max_blocks_per_seq << a.block_shift);
+    int4 rec = make_int4(0, 0, 0, 0);
+    if (m.chunked) rec = *reinterpret_cast<const int4*>(a.part_n + 4 * (int64_t)s);
     if (L <= 0) {
         m.n = 0;
         m.base = 0;
@@ -399,11 +428,12 @@ __device__ __forceinline__ MergeList merge_list(const DecodeArgs& a, int s) {
         m.n = (L + a.partition - 1) / a.partition;
         m.base = (int64_t)s * a.max_partitions;
     } else {
-        // as the attention pass recorded it, kept within the workspace
-        const int32_t* h = a.part_n + 4 * (int64_t)s;
-        const int first = min(max(h[1], 0), a.max_chunks - 1);
-        m.n = min(max(h[0], 0), a.max_chunks - first);
-        m.base = 2 * (int64_t)first + (h[2] & 1);
+        // as the attention pass recorded it (first chunk, slot there, last
+        // chunk), kept within the workspace
+        const int first = min(max(rec.y, 0), a.max_chunks - 1);
+        const int last = min(max(rec.x, first), a.max_chunks - 1);
+        m.n = last - first + 1;
+        m.base = 2 * (int64_t)first + (rec.z & 1);
     }
     return m;
 }

@@ -34,6 +34,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kMaxPartition = 1 << 20;
 
+// Token chunks dealt to an odd-numbered XCD, in 16ths of an even one's (see
+// ChunkLayout in decode_common.h).
+constexpr int kOddXcdWeight = 16;
+
 }  // namespace
 
 DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size, int block_size) {
@@ -47,6 +51,7 @@ DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size, 
     g.row_lanes = head_dim * g.kv_bytes / 16;
     g.rows = g.mfma ? kDecodeWaves : 64 / g.row_lanes;
     g.elems = 16 / g.kv_bytes;
+    g.max_per_cu = g.mfma ? 2 : 8;
     return g;
 }
 
@@ -113,10 +118,14 @@ bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
         if (part < block_size) part = block_size;
         p.run_partition = (part + block_size - 1) / block_size * block_size;
     }
-    // token chunks: at least 64 tokens (whole blocks) each, and never more
-    // chunks than the GPU holds workgroups at once
+    // token chunks: at least 64 tokens (whole blocks) each, never more chunks
+    // than the GPU holds workgroups at once, nor than the batch's tokens fill
     p.part_min = (64 + block_size - 1) / block_size * block_size;
-    p.max_chunks = std::max(1, slot_cap() / p.groups);
+    {
+        const int64_t by_slots = std::max<int64_t>(1, (int64_t)device_cus() * p.geo.max_per_cu / p.groups);
+        const int64_t by_tokens = std::max<int64_t>(1, ((int64_t)num_seqs * max_tokens + p.part_min - 1) / p.part_min);
+        p.max_chunks = (int)std::min(by_slots, by_tokens);
+    }
     int64_t slots;                                   // partial-result slots the workspace holds
     if (partition_size > 0) {
         p.partition = partition_size;
@@ -176,10 +185,10 @@ int current_cus(int* dev_out) {
 
 }  // namespace
 
-int slot_cap() {
+int device_cus() {
     int dev = 0;
     const int cus = current_cus(&dev);
-    return cus > 0 ? 8 * cus : 2048;
+    return cus > 0 ? cus : 256;
 }
 
 int resident_workgroups(const void* kernel, size_t dyn_lds) {
@@ -487,13 +496,16 @@ pa_status pa_copy_blocks(const void* src_pool, int32_t src_num_blocks, void* dst
     return launch_copy_blocks(a, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
-static pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
-                    pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
-                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
-                    float scale, float k_scale, float v_scale, int32_t partition_size,
-                    void* workspace, size_t workspace_bytes, void* stream,
-                    const void* new_key = nullptr, const void* new_value = nullptr, int32_t run_size = 1) {
+}  // extern "C"
+
+namespace pa {
+pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
+                        pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        float scale, float k_scale, float v_scale, int32_t partition_size,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        const void* new_key, const void* new_value, int32_t run_size) {
     pa_status st = check_decode_args(out, query, q_dtype, kv_pool, kv_dtype, block_tables,
                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                                      block_size, max_blocks_per_seq, num_blocks, scale, k_scale,
@@ -534,6 +546,7 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
     a.part_min = plan.part_min;
     a.max_chunks = plan.max_chunks;
     a.target_items = plan.max_chunks * plan.groups;    // the launcher sets it from the kernel's occupancy
+    a.odd_xcd_weight = kOddXcdWeight;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;
     a.new_key = new_key;
@@ -552,6 +565,9 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
                                   phases, stream);
     return err == 0 ? PA_OK : PA_ERR_HIP;
 }
+}  // namespace pa
+
+extern "C" {
 
 #define PA_DECODE_PARAMS                                                                          \
     void *out, const void *query, pa_dtype q_dtype, const void *kv_pool, pa_dtype kv_dtype,       \
@@ -564,9 +580,15 @@ static pa_status decode_phases(int phases, void* out, const void* query, pa_dtyp
         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, \
         partition_size, workspace, workspace_bytes, stream
 
-pa_status pa_decode(PA_DECODE_PARAMS) { return decode_phases(kPhasePartials | kPhaseMerge, PA_DECODE_ARGS); }
-pa_status pa_decode_partials(PA_DECODE_PARAMS) { return decode_phases(kPhasePartials, PA_DECODE_ARGS); }
-pa_status pa_decode_merge(PA_DECODE_PARAMS) { return decode_phases(kPhaseMerge, PA_DECODE_ARGS); }
+pa_status pa_decode(PA_DECODE_PARAMS) {
+    return decode_phases(kPhasePartials | kPhaseMerge, PA_DECODE_ARGS, nullptr, nullptr, 1);
+}
+pa_status pa_decode_partials(PA_DECODE_PARAMS) {
+    return decode_phases(kPhasePartials, PA_DECODE_ARGS, nullptr, nullptr, 1);
+}
+pa_status pa_decode_merge(PA_DECODE_PARAMS) {
+    return decode_phases(kPhaseMerge, PA_DECODE_ARGS, nullptr, nullptr, 1);
+}
 
 // pa_decode with the newest tokens' K/V written by the attention pass itself
 static pa_status check_write_source(int32_t num_seqs, pa_dtype q_dtype, const void* key, const void* value,

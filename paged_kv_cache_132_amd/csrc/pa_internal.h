@@ -28,6 +28,11 @@ struct DecodeGeometry {
     int row_lanes;   // lanes per KV-head row (vector kernel)
     int rows;        // KV heads per workgroup
     int elems;       // KV elements per lane per token (vector kernel)
+    // most workgroups of the attention kernel one compute unit holds: 2 for
+    // the matrix-core kernels (registers or LDS allow no more), 8 (the
+    // hardware's wave limit) for the vector kernel.  It bounds the token
+    // chunks the workspace has room for; a launch never makes more chunks.
+    int max_per_cu;
 };
 
 bool gqa_mfma_supported(pa_dtype q_dtype, pa_dtype kv_dtype, int head_dim, int group_size);
@@ -84,6 +89,7 @@ struct DecodeArgs {
     // token chunks (partition == 0): shortest chunk, most chunks, and the
     // workgroups the attention kernel keeps resident on the whole GPU
     int32_t part_min, max_chunks, target_items;
+    int32_t odd_xcd_weight;  // token chunks: length of an odd XCD's chunks, in 16ths of an even one's
     float score_scale;      // scale * k_scale * log2(e): scores in the exp2 domain
     float v_scale;
     // Fused cache write (null: none): the newest token's K/V rows
@@ -141,15 +147,24 @@ struct CopyArgs {
 
 // Workgroups of kDecodeThreads threads (and `dyn_lds` bytes of dynamic LDS)
 // of `kernel` the current device holds at once: compute units x resident
-// workgroups per unit, at most slot_cap().  Cached per (device, kernel).
+// workgroups per unit (at most 8 per unit).  Cached per (device, kernel).
 int resident_workgroups(const void* kernel, size_t dyn_lds);
-// Most workgroups of kDecodeThreads threads any kernel can keep resident on
-// the current device (8 per compute unit); 2048 when the device cannot be
-// asked.
-int slot_cap();
+// Compute units of the current device; 256 (MI355X) when the device cannot
+// be asked.
+int device_cus();
 // Workgroups a decode launch needs for the plan; with token chunks it also
 // sets a->target_items for `kernel`.
 int64_t decode_grid(DecodeArgs* a, const DecodePlan& plan, const void* kernel, size_t dyn_lds);
+
+// pa_decode and its variants: argument checks, plan and launches of the
+// given phases (kPhasePartials, kPhaseMerge) with the given workspace.
+pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
+                        pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        float scale, float k_scale, float v_scale, int32_t partition_size,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        const void* new_key, const void* new_value, int32_t run_size);
 
 // Launchers (defined next to their kernels).  Return the hipError_t as int.
 // phase bit 1: attention pass (partials), bit 2: split-K merge.
