@@ -396,6 +396,35 @@ pa_status pa_copy_blocks(const void* src_pool, int32_t src_num_blocks, void* dst
                          int32_t num_kv_heads, int32_t head_dim, const int32_t* block_mapping,
                          int32_t num_pairs, void* stream);
 
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The split-K workspace is a fixed array inside the
+ * library, one copy per GPU, held until the process ends; the call itself
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ *   Arguments, results and errors are those of pa_decode without the
+ *   workspace; partition_size 0 or a positive multiple of block_size.
+ *   PA_ERR_WORKSPACE_TOO_SMALL when the call needs more workspace than the
+ *   array holds: pa_decode_workspace_size(...) > pa_decode_noalloc_max_workspace()
+ *   (64 MiB).  PA_ERR_HIP if the array's device address cannot be found.
+ *
+ * Every call on one GPU uses that GPU's one array, whose contents the last
+ * call left (no call needs them cleared): calls that may overlap on one GPU
+ * -- on different streams, or from different threads -- race on it and
+ * must be ordered by the caller.
+ */
+pa_status pa_decode_noalloc(void* out, const void* query, pa_dtype q_dtype,
+                            const void* kv_pool, pa_dtype kv_dtype,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                            float scale, float k_scale, float v_scale, int32_t partition_size,
+                            void* stream);
+
+/* Bytes of the fixed workspace pa_decode_noalloc uses on each GPU. */
+size_t pa_decode_noalloc_max_workspace(void);
+
 /* Human-readable name of a status value (static storage, never NULL). */
 const char* pa_status_string(pa_status status);
 

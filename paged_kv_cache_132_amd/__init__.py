@@ -5,6 +5,7 @@ in include/pa.h); this package is its thin Python binding:
 
     cache_write(kv_pool, key, value, block_tables, context_lens, k_scale, v_scale)
     decode(query, kv_pool, block_tables, context_lens, scale, k_scale, v_scale, ...)
+    decode_noalloc(query, kv_pool, block_tables, context_lens, scale, k_scale, v_scale, out=...)
     cache_write_tokens(kv_pool, key, value, block_tables, context_lens, cu_seqlens, k_scale, v_scale)
     prefill(query, kv_pool, block_tables, context_lens, cu_seqlens, scale, k_scale, v_scale)
     copy_blocks(src_pool, dst_pool, block_mapping)
@@ -22,6 +23,7 @@ from ._lib import (
     cache_write_tokens,
     copy_blocks,
     decode,
+    decode_noalloc,
     decode_partition_size,
     decode_workspace_size,
     load,
@@ -31,5 +33,5 @@ from ._lib import (
 
 __all__ = [
     "PA_F16", "PA_BF16", "PA_FP8_E4M3", "EXPORTED", "LIB_PATH", "Workspace", "cache_write", "cache_write_tokens", "copy_blocks", "decode",
-    "decode_partition_size", "decode_workspace_size", "load", "pa_dtype", "prefill",
+    "decode_noalloc", "decode_partition_size", "decode_workspace_size", "load", "pa_dtype", "prefill",
 ]

@@ -24,7 +24,8 @@ STATUS_NAMES = {
 EXPORTED = ("pa_cache_write", "pa_cache_write_tokens", "pa_copy_blocks", "pa_decode", "pa_decode_partials",
             "pa_decode_merge", "pa_decode_write", "pa_decode_write_partials", "pa_decode_shared",
             "pa_decode_write_partials_shared", "pa_decode_workspace_size",
-            "pa_decode_partition_size", "pa_prefill", "pa_prefill_write", "pa_status_string",
+            "pa_decode_partition_size", "pa_decode_noalloc", "pa_decode_noalloc_max_workspace",
+            "pa_prefill", "pa_prefill_write", "pa_status_string",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
             "pa_bm_free_sequence", "pa_bm_take_copies", "pa_bm_sequence_length", "pa_bm_block_table",
             "pa_bm_ref_count", "pa_bm_stats_get")
@@ -69,6 +70,11 @@ def load() -> ctypes.CDLL:
         lib.pa_decode_write_partials_shared.argtypes = lib.pa_decode_write_partials.argtypes + [i32]
         lib.pa_decode_workspace_size.restype = sz
         lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
+        lib.pa_decode_noalloc.restype = ctypes.c_int
+        lib.pa_decode_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                          i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, vp]
+        lib.pa_decode_noalloc_max_workspace.restype = sz
+        lib.pa_decode_noalloc_max_workspace.argtypes = []
         lib.pa_decode_partition_size.restype = i32
         lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
         i64, u64, ip = ctypes.c_int64, ctypes.c_uint64, ctypes.POINTER(ctypes.c_int32)
@@ -349,3 +355,27 @@ def decode(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tenso
             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream), *extra)
     _check(st, f"pa_decode ({phase})")
     return out
+
+
+def decode_noalloc(query: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                   out: torch.Tensor | None = None, partition_size: int = 0, stream=None) -> torch.Tensor:
+    """pa_decode_noalloc: paged decode with the library's fixed per-GPU
+    workspace (the C call allocates nothing; pass `out` to allocate nothing
+    here either).  Calls that may overlap on one GPU must be ordered."""
+    nb, bs, hkv, d = _pool_dims(kv_pool)
+    if query.dim() != 3 or query.shape[2] != d or not query.is_contiguous():
+        raise ValueError("query must be a contiguous [num_seqs, num_heads, head_dim] tensor")
+    B, hq = int(query.shape[0]), int(query.shape[1])
+    mb = _tables(block_tables, context_lens, B)
+    if out is None:
+        out = torch.empty_like(query)
+    elif out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
+        raise ValueError("out must match query")
+    st = load().pa_decode_noalloc(_ptr(out), _ptr(query), pa_dtype(query), _ptr(kv_pool), pa_dtype(kv_pool),
+                                  _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, mb, nb,
+                                  float(scale), float(k_scale), float(v_scale), int(partition_size),
+                                  _stream(stream))
+    _check(st, "pa_decode_noalloc")
+    return out
+

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libpa.so")
 BENCH_LIB = os.path.join(PKG, "libpa_bench.so")
 
 SOURCES = ["pa_api.cpp", "block_manager.cpp", "cache_write.hip", "copy_blocks.hip", "decode.hip",
-           "decode_gqa_mfma.hip", "decode_gqa16_mfma.hip", "prefill.hip"]
+           "decode_gqa_mfma.hip", "decode_gqa16_mfma.hip", "decode_noalloc.hip", "prefill.hip"]
 BENCH_SOURCES = ["bench_util.hip"]
 
 COMPILE_FLAGS = [

@@ -323,3 +323,33 @@ def test_prefill_write_without_tokens_is_a_noop(lib):
     assert call_prefill_write(lib, max_new_tokens=0, cu_seqlens=None, key=None, value=None) == 0
     assert call_prefill_write(lib, num_tokens=0, cu_seqlens=None, key=None, value=None, q_dtype=BF16,
                               kv_dtype=FP8, src_dtype=BF16) == 0
+
+
+def call_noalloc(lib, **kw):
+    a = decode_args(**kw)
+    return lib.pa_decode_noalloc(a["out"], a["query"], a["q_dtype"], a["kv_pool"], a["kv_dtype"],
+                                 a["block_tables"], a["context_lens"], a["num_seqs"], a["num_heads"],
+                                 a["num_kv_heads"], a["head_dim"], a["block_size"], a["max_blocks_per_seq"],
+                                 a["num_blocks"], a["scale"], a["k_scale"], a["v_scale"], a["partition_size"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), NULLP),
+    (dict(kv_pool=None), NULLP),
+    (dict(q_dtype=F16, kv_dtype=BF16), UNSUP),
+    (dict(head_dim=96), UNSUP),
+    (dict(partition_size=24), SHAPE),
+    (dict(query=FAKE + 4), MISAL),
+    # a workspace beyond the fixed 64 MiB array: refused before any device call
+    (dict(num_seqs=4096, num_heads=64, num_kv_heads=64, head_dim=128, max_blocks_per_seq=4096,
+          partition_size=16), WS),
+])
+def test_decode_noalloc_rejects_bad_arguments(lib, kw, status):
+    assert lib.pa_decode_noalloc_max_workspace() == 64 << 20
+    assert call_noalloc(lib, **kw) == status
+
+
+def test_decode_noalloc_zero_sequences_is_a_noop(lib):
+    assert call_noalloc(lib, num_seqs=0, out=None, query=None) == OK
+
