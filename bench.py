@@ -61,8 +61,13 @@ def algorithmic_bytes(b) -> dict:
     tables = 4 * int(np.sum(-(-lens // bs))) + 4 * B
     decode = kv + qo + tables
     write = B * 2 * Hkv * D * (ELEM[b.src_dtype] + ELEM[b.kv_dtype]) + 4 * B + 4 * B
-    unique_kv = b.unique_blocks_in_use() * 2 * bs * Hkv * D * ELEM[b.kv_dtype]
-    return {"kv": kv, "decode": decode, "write": write, "unique_kv_blocks": unique_kv}
+    out = {"kv": kv, "decode": decode, "write": write}
+    if b.notes.get("prefix_blocks"):
+        # a batch that shares prefix blocks: each stored token once (the HBM floor)
+        unique_kv = b.unique_tokens_in_use() * 2 * Hkv * D * ELEM[b.kv_dtype]
+        out["unique_kv"] = unique_kv
+        out["unique_decode"] = unique_kv + qo + tables
+    return out
 
 
 # the sources the decode kernels and their launcher are built from, and the
@@ -233,6 +238,7 @@ def cpu_baseline(b, budget_s: float = 20.0) -> dict:
         "value": round(kv_bytes / t_total / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
+        "host_cores_available": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{len(done)} sequence decodes ({len(done) / b.num_seqs:.2f} passes over the "
                   f"{b.num_seqs}-sequence batch, {tokens} context tokens), float64 numpy, {t_total:.1f} s",
@@ -436,16 +442,27 @@ def run_decode(args, torch, pa, b) -> dict:
     dev = upload(b, torch, pa, copies)
     kvt = pa.pa_dtype(dev["pools"][0])
     mb = b.max_blocks_per_seq
+    partition_size = args.partition_size
+    run_size = int(args.run_size)
+    if b.notes.get("prefix_blocks") and args.run_size is None and args.partition_size is None:
+        # the shared-prefix batch: shared runs as long as a share group, and a
+        # partition that tiles the shared prefix exactly (4480 = 5 x 896) so
+        # no shared block falls to the per-sequence kernel
+        run_size = int(b.notes.get("share_group", 1))
+        partition_size = int(b.notes["prefix_tokens"]) // 5
+    partition_size = partition_size or 0
+    run_size = run_size or 1
     partition = pa.decode_partition_size(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.block_size,
-                                         mb, kvt, args.partition_size)
+                                         mb, kvt, partition_size)
+    if partition_size == 0:
+        partition = f"token chunks (>= {partition})"
     ws = torch.zeros(pa.decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim,
-                                              b.block_size, mb, kvt, args.partition_size),
+                                              b.block_size, mb, kvt, partition_size),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
 
     fused = not args.separate_write and b.q_dtype == b.src_dtype
-    run_size = int(args.run_size)
     if run_size != 1 and not fused:
         raise SystemExit("--run-size takes the fused step (pa_decode_write_partials_shared)")
 
@@ -455,7 +472,7 @@ def run_decode(args, torch, pa, b) -> dict:
         # the attention pass; otherwise pa_cache_write runs first.
         pool = dev["pools"][i % copies]
         dargs = (dev["q"], pool, dev["bt"], dev["lens"], b.scale, b.k_scale, b.v_scale)
-        dkw = dict(out=out, workspace=ws, partition_size=args.partition_size)
+        dkw = dict(out=out, workspace=ws, partition_size=partition_size)
         if ev is not None:
             ev[0].record(stream)
         if not fused:
@@ -535,10 +552,14 @@ def run_decode(args, torch, pa, b) -> dict:
     ms_step = graph_ms_step if graph_ms_step is not None else eager_ms_step
     attn_us = float(attn_ms.mean() * 1e3)
     call_us = float(call_ms.mean() * 1e3)
-    # the attention kernel's algorithmic bytes: the decode's, plus the write's when fused
-    attn_bytes = nbytes["decode"] + (nbytes["write"] if fused else 0)
+    # the attention kernel's algorithmic bytes: the decode's, plus the write's
+    # when fused.  A batch that shares prefix blocks counts each stored token
+    # once (its HBM floor); the logical bytes, every sequence's own tokens,
+    # are reported beside.
+    decode_bytes = nbytes.get("unique_decode", nbytes["decode"])
+    attn_bytes = decode_bytes + (nbytes["write"] if fused else 0)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
-    step_bytes = nbytes["decode"] + nbytes["write"]
+    step_bytes = decode_bytes + nbytes["write"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"attention pass mean {attn_us:.1f} us (p10 {np.percentile(attn_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(attn_ms, 90) * 1e3:.1f}); merge {merge_ms.mean() * 1e3:.1f} us; "
@@ -598,8 +619,10 @@ def run_decode(args, torch, pa, b) -> dict:
         },
         "algorithmic_bytes": nbytes,
     }
-    if b.notes.get("prefix_blocks"):
-        res["unique_kv_gbs"] = round(nbytes["unique_kv_blocks"] / (attn_us * 1e-6) / 1e9, 1)
+    if "unique_decode" in nbytes:
+        res["bytes_basis"] = "unique (each stored token once)"
+        logical = nbytes["decode"] + (nbytes["write"] if fused else 0)
+        res["logical_kv_gbs"] = round(logical / (attn_us * 1e-6) / 1e9, 1)
     return res
 
 
@@ -719,10 +742,12 @@ def main() -> int:
                          "prefill: the prompt stage (multi-token write + causal prefill); "
                          "block_sizes: the decode step at block sizes 8, 16, 32; "
                          "block_manager: the host block manager (CPU only)")
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="tokens per split-K partition; 0: token chunks (the library's choice, the default "
+                         "except for the shared-prefix batch, which takes 896 with runs of 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--run-size", type=int, default=1,
+    ap.add_argument("--run-size", type=int, default=None,
                     help="decode step: sequences share prefix blocks in aligned runs of this many "
                          "(pa_decode_write_partials_shared; 1, 2, 4 or 8)")
     ap.add_argument("--separate-write", action="store_true",

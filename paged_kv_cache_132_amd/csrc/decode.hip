@@ -587,8 +587,8 @@ int launch_decode(const DecodeArgs& a, const DecodePlan& plan, pa_dtype q_dtype,
         else err = launch_t<PA_BF16, PA_FP8_E4M3>(a, plan, head_dim, group_size, st);
     }
     // no merge when no sequence can be split: one fixed partition holds every
-    // table, or a single chunk the whole batch
-    const bool can_split = a.partition > 0 ? plan.max_partitions > 1 : plan.max_chunks > 1;
+    // table, and (partition 0) a single chunk the whole batch
+    const bool can_split = plan.max_partitions > 1 || (a.partition == 0 && plan.max_chunks > 1);
     if (err != 0 || !(phases & kPhaseMerge) || !can_split) return err;
     const bool f16 = q_dtype == PA_F16;
     if (head_dim == 64) return f16 ? launch_merge<PA_F16, 64>(a, st) : launch_merge<PA_BF16, 64>(a, st);

@@ -289,14 +289,21 @@ __device__ inline bool next_chunk_segment(const DecodeArgs& a, WorkItem& w) {
 // a partition p, and the item's sequence is one of them, in order.
 // Each wave computes this on its own -- no LDS, no barriers -- so waves of a
 // workgroup may call it independently; they all reach the same answer.
-__device__ inline bool begin_partition_work(const DecodeArgs& a, int wg, WorkItem& w) {
+//
+// With partition 0 this is the layout of batches that share prefix blocks:
+// there the sharers of a block must read it at about the same time, and
+// fixed partitions restart them together at every partition.
+__device__ __forceinline__ int fixed_partition(const DecodeArgs& a) {
+    return a.partition > 0 ? a.partition : a.fallback_partition;
+}
+
+__device__ inline bool begin_partition_work(const DecodeArgs& a, int wg, WorkItem& w, bool shares) {
     constexpr int kCached = kCachedChunks;
     const int lane = threadIdx.x & 63;
     const int B = a.num_seqs;
     const int P = a.max_partitions;
-    const int T = a.partition;
+    const int T = fixed_partition(a);
     const int max_tokens = a.max_blocks_per_seq << a.block_shift;
-    const bool shares = batch_shares_prefix(a);                   // its loads go out with the lengths'
     int len_raw[kCached];
     load_lengths(a, len_raw);
     int cached[kCached];
@@ -374,14 +381,22 @@ __device__ inline bool begin_partition_work(const DecodeArgs& a, int wg, WorkIte
     return true;
 }
 
-// The first segment of workgroup `wg` of a per-sequence decode kernel.
+// Whether a launch with partition 0 lays out token chunks: unless the batch
+// shares prefix blocks (then fixed partitions of fallback_partition tokens).
+__device__ __forceinline__ bool uses_chunks(const DecodeArgs& a, bool shares) {
+    return a.partition == 0 && !shares;
+}
+
+// The first segment of workgroup `wg` of a per-sequence decode kernel.  (The
+// grid covers both layouts; workgroups past the chosen one's items leave.)
 __device__ __forceinline__ bool begin_work(const DecodeArgs& a, int wg, WorkItem& w) {
-    return a.partition > 0 ? begin_partition_work(a, wg, w) : begin_chunk_work(a, wg, w);
+    const bool shares = batch_shares_prefix(a);                   // its loads go out with the lengths'
+    return uses_chunks(a, shares) ? begin_chunk_work(a, wg, w) : begin_partition_work(a, wg, w, shares);
 }
 
 // Advance to the workgroup's next segment; false when it has none.
 __device__ __forceinline__ bool next_segment(const DecodeArgs& a, WorkItem& w) {
-    return a.partition > 0 ? false : next_chunk_segment(a, w);
+    return w.chunk >= 0 ? next_chunk_segment(a, w) : false;
 }
 
 // Whether the segment is its sequence's whole range (the output is written
@@ -394,7 +409,7 @@ __device__ __forceinline__ bool whole_sequence(const WorkItem& w) { return w.t0 
 // one that holds its last token records that chunk.  Thread 0, once per
 // sequence and call.
 __device__ __forceinline__ void publish_segments(const DecodeArgs& a, const WorkItem& w) {
-    if (a.partition > 0 || w.group != 0 || threadIdx.x != 0) return;
+    if (w.chunk < 0 || w.group != 0 || threadIdx.x != 0) return;
     int32_t* h = a.part_n + 4 * (int64_t)w.s;
     if (w.t0 == 0) {
         h[1] = w.chunk;
@@ -416,7 +431,7 @@ struct MergeList {
 
 __device__ __forceinline__ MergeList merge_list(const DecodeArgs& a, int s) {
     MergeList m;
-    m.chunked = a.partition == 0;
+    m.chunked = uses_chunks(a, batch_shares_prefix(a));
     // the length and (token chunks) the record of the attention pass, loaded together
     const int L = min(a.context_lens[s], a.max_blocks_per_seq << a.block_shift);
     int4 rec = make_int4(0, 0, 0, 0);
@@ -425,7 +440,8 @@ __device__ __forceinline__ MergeList merge_list(const DecodeArgs& a, int s) {
         m.n = 0;
         m.base = 0;
     } else if (!m.chunked) {
-        m.n = (L + a.partition - 1) / a.partition;
+        const int T = fixed_partition(a);
+        m.n = (L + T - 1) / T;
         m.base = (int64_t)s * a.max_partitions;
     } else {
         // as the attention pass recorded it (first chunk, slot there, last

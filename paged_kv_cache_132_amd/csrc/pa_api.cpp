@@ -217,7 +217,11 @@ int64_t decode_grid(DecodeArgs* a, const DecodePlan& plan, const void* kernel, s
     if (slots <= 0) slots = plan.max_chunks * plan.groups;
     slots = std::min(slots, plan.max_chunks * plan.groups);
     a->target_items = slots;
-    return (int64_t)std::max(slots / plan.groups, 1) * plan.groups;
+    // enough workgroups for the chunks, or for the fixed partitions a batch
+    // that shares prefix blocks takes instead (those past the layout's items
+    // leave at once, in slots the others have freed)
+    const int64_t fixed = (int64_t)plan.groups * a->num_seqs * plan.max_partitions;
+    return std::max<int64_t>((int64_t)std::max(slots / plan.groups, 1) * plan.groups, fixed);
 }
 
 }  // namespace pa
@@ -547,6 +551,7 @@ pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dty
     a.max_chunks = plan.max_chunks;
     a.target_items = plan.max_chunks * plan.groups;    // the launcher sets it from the kernel's occupancy
     a.odd_xcd_weight = kOddXcdWeight;
+    a.fallback_partition = plan.run_partition;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;
     a.new_key = new_key;

@@ -89,6 +89,9 @@ struct DecodeArgs {
     // token chunks (partition == 0): shortest chunk, most chunks, and the
     // workgroups the attention kernel keeps resident on the whole GPU
     int32_t part_min, max_chunks, target_items;
+    // partition 0 with a batch that shares prefix blocks, or shared runs:
+    // the fixed partition taken instead
+    int32_t fallback_partition;
     int32_t odd_xcd_weight;  // token chunks: length of an odd XCD's chunks, in 16ths of an even one's
     float score_scale;      // scale * k_scale * log2(e): scores in the exp2 domain
     float v_scale;

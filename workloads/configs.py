@@ -127,6 +127,15 @@ class PagedBatch:
     def unique_blocks_in_use(self) -> int:
         return int(len({b for tab in self.tables for b in tab}))
 
+    def unique_tokens_in_use(self) -> int:
+        """Distinct (block, offset) slots some sequence reads: the tokens a
+        batch that shares prefix blocks stores once."""
+        slots = set()
+        for tab, L in zip(self.tables, self.context_lens):
+            for t in range(int(L)):
+                slots.add((int(tab[t // self.block_size]), t % self.block_size))
+        return len(slots)
+
 
 def _build(
     name: str,
@@ -231,7 +240,7 @@ def _build(
         kv_pool=kv_pool, kv_source=kv_source, new_key=new_key,
         new_value=new_value, step_query=step_query,
         notes={"used_blocks": int(used), "prefix_blocks": int(prefix_blocks),
-               "share_group": int(share_group)},
+               "prefix_tokens": int(prefix_blocks * bs), "share_group": int(share_group)},
     )
 
 
