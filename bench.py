@@ -443,7 +443,7 @@ def run_decode(args, torch, pa, b) -> dict:
     kvt = pa.pa_dtype(dev["pools"][0])
     mb = b.max_blocks_per_seq
     partition_size = args.partition_size
-    run_size = int(args.run_size)
+    run_size = args.run_size
     if b.notes.get("prefix_blocks") and args.run_size is None and args.partition_size is None:
         # the shared-prefix batch: shared runs as long as a share group, and a
         # partition that tiles the shared prefix exactly (4480 = 5 x 896) so
