@@ -13,32 +13,15 @@ namespace pa {
 
 constexpr int kXcds = 8;                          // accelerator complex dies of the chip
 
-// Where the chunks lie.  Chunk c's work items (one per KV-head group) go to
-// the XCD that the renumbering below gives item c * groups; an XCD with an
-// odd index gets chunks odd_xcd_weight/16 as long as an even one's (the odd
-// XCDs of this part stream measurably slower, whichever tokens they get).
-// Chunk boundaries are whole blocks: chunk c starts at block
-// floor(units * W(c) / W(n)), W(c) the weight of chunks 0 .. c-1.
+// Where the chunks lie: chunk c starts at block floor(c * units / n) of the
+// padded batch, so chunks differ in length by at most one block.  (Odd XCDs
+// of this part stream about 8 % slower than even ones whichever chunks they
+// get, but chunks weighted by XCD did not shorten the kernel.)
 struct ChunkLayout {
-    int n, units, groups, per, rem, block_size, w_odd;
-
-    // first chunk whose first item the renumbering gives XCD x (x = 0 .. 8)
-    __device__ __forceinline__ int first_chunk(int x) const {
-        const int64_t i = (int64_t)x * per + min(x, rem);
-        return (int)((i + groups - 1) / groups);
-    }
-    __device__ __forceinline__ int64_t weight_before(int c) const {
-        int64_t W = 0;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const int f0 = first_chunk(x), f1 = first_chunk(x + 1);
-            W += (int64_t)((x & 1) ? w_odd : 16) * max(0, min(c, f1) - f0);
-        }
-        return W;
-    }
+    int n, units, block_size;
     // first padded token of chunk c (c = 0 .. n)
     __device__ __forceinline__ int start(int c) const {
-        return (int)((int64_t)units * weight_before(c) / weight_before(n)) * block_size;
+        return (int)((int64_t)c * units / n) * block_size;
     }
 };
 
@@ -60,12 +43,6 @@ struct WorkItem {
     int chunk, pos, end, off;
     int64_t seg_slot;   // partial-result slot of this segment (times num_heads, plus the head)
 };
-
-// The chunk layout of a launch with n chunks over `units` blocks.
-__device__ __forceinline__ ChunkLayout chunk_layout(const DecodeArgs& a, int n, int units) {
-    const int items = n * a.groups;
-    return ChunkLayout{n, units, a.groups, items / kXcds, items % kXcds, a.block_size, a.odd_xcd_weight};
-}
 
 constexpr int kCachedChunks = 8;                  // sequences 0..511 keep their length in registers
 
@@ -226,10 +203,9 @@ __device__ inline bool begin_chunk_work(const DecodeArgs& a, int wg, WorkItem& w
     const int item = x * per + min(x, rem) + j;
     w.chunk = item / a.groups;
     w.group = item % a.groups;
-    const ChunkLayout layout = chunk_layout(a, n, units);
+    const ChunkLayout layout{n, units, U};
     w.pos = layout.start(w.chunk);
     w.end = layout.start(w.chunk + 1);
-    if (w.end <= w.pos) return false;                             // a chunk the weights left empty
     // the sequence holding the chunk's first token: the last s with
     // offset(s) <= pos (offsets grow strictly: every sequence takes a block)
     int lo = 0, hi = B;                                           // offset(lo) <= pos < offset(hi)

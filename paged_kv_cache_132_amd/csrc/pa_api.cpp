@@ -34,10 +34,6 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kMaxPartition = 1 << 20;
 
-// Token chunks dealt to an odd-numbered XCD, in 16ths of an even one's (see
-// ChunkLayout in decode_common.h).
-constexpr int kOddXcdWeight = 16;
-
 }  // namespace
 
 DecodeGeometry decode_geometry(int head_dim, pa_dtype kv_dtype, int group_size, int block_size) {
@@ -550,7 +546,6 @@ pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dty
     a.part_min = plan.part_min;
     a.max_chunks = plan.max_chunks;
     a.target_items = plan.max_chunks * plan.groups;    // the launcher sets it from the kernel's occupancy
-    a.odd_xcd_weight = kOddXcdWeight;
     a.fallback_partition = plan.run_partition;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;

@@ -92,7 +92,6 @@ struct DecodeArgs {
     // partition 0 with a batch that shares prefix blocks, or shared runs:
     // the fixed partition taken instead
     int32_t fallback_partition;
-    int32_t odd_xcd_weight;  // token chunks: length of an odd XCD's chunks, in 16ths of an even one's
     float score_scale;      // scale * k_scale * log2(e): scores in the exp2 domain
     float v_scale;
     // Fused cache write (null: none): the newest token's K/V rows
