@@ -473,8 +473,14 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
             const int64_t slot = list.slot(min(i0 + k, list.n - 1)) * a.num_heads + h;
             mp[k] = a.part_ml[slot * 2];
             lp[k] = a.part_ml[slot * 2 + 1];
+            const float* po = a.part_o + slot * D + d0;
+            if constexpr (NE == 4) {
+                const float4 v = *reinterpret_cast<const float4*>(po);
+                op[k][0] = v.x; op[k][1] = v.y; op[k][2] = v.z; op[k][3] = v.w;
+            } else {
 #pragma unroll
-            for (int e = 0; e < NE; ++e) op[k][e] = a.part_o[slot * D + d0 + e];
+                for (int e = 0; e < NE; ++e) op[k][e] = po[e];
+            }
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
@@ -496,16 +502,23 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
 
 // Second pass of split-K: one thread per output element of every sequence
 // whose range was split between workgroups.
+// A workgroup takes kMergeHeads query heads of one sequence, a thread NE
+// consecutive output elements of one head (16-byte loads of the partial o at
+// head_dim 128): few workgroups, most of which leave after one load when
+// their sequence was not split.
+constexpr int kMergeHeads = 8;
+
 template <int QT, int D>
 __global__ __launch_bounds__(kDecodeThreads) void merge_kernel(DecodeArgs a) {
-    constexpr int HPB = kDecodeThreads / D;          // query heads per workgroup
-    const int chunks = (a.num_heads + HPB - 1) / HPB;
+    constexpr int NE = kMergeHeads * D / kDecodeThreads;   // output elements per thread
+    constexpr int TPH = D / NE;                            // threads per head
+    const int chunks = (a.num_heads + kMergeHeads - 1) / kMergeHeads;
     const int s = blockIdx.x / chunks;
-    const int h = (blockIdx.x % chunks) * HPB + threadIdx.x / D;
-    const int d = threadIdx.x % D;
+    const int h = (blockIdx.x % chunks) * kMergeHeads + threadIdx.x / TPH;
+    const int d0 = (threadIdx.x % TPH) * NE;
     const MergeList list = merge_list(a, s);
     if (list.n <= 1 || h >= a.num_heads) return;
-    merge_partials<QT, D, 1>(a, s, h, d, list);
+    merge_partials<QT, D, NE>(a, s, h, d0, list);
 }
 
 template <int QT, int KVT, int D>
@@ -552,7 +565,7 @@ int launch_run_t(const DecodeArgs& a, int head_dim, hipStream_t st) {
 
 template <int QT, int D>
 int launch_merge(const DecodeArgs& a, hipStream_t st) {
-    const int chunks = (a.num_heads + kDecodeThreads / D - 1) / (kDecodeThreads / D);
+    const int chunks = (a.num_heads + kMergeHeads - 1) / kMergeHeads;
     hipLaunchKernelGGL((merge_kernel<QT, D>), dim3((unsigned)(a.num_seqs * chunks)), dim3(kDecodeThreads), 0, st, a);
     return (int)hipGetLastError();
 }
