@@ -325,7 +325,8 @@ pa_status pa_cache_write_tokens(void* kv_pool, pa_dtype kv_dtype, const void* ke
  *   context_lens  lengths with the new tokens included; the n_s new queries
  *                 of sequence s sit at positions L_s - n_s .. L_s - 1 and
  *                 query i attends to keys 0 .. L_s - n_s + i.
- *   max_new_tokens  an upper bound on every n_s (sizes the launch grid).
+ *   max_new_tokens  an upper bound on every n_s (sizes the launch grid); a
+ *                 sequence with n_s > max_new_tokens produces no output rows.
  *   The pool must already hold the new tokens (pa_cache_write_tokens first,
  *   on the same stream).
  * No workspace.  Supported combinations, scales and errors as in pa_decode;

@@ -351,7 +351,8 @@ static pa_status check_prefill_args(const void* out, const void* query, pa_dtype
     if ((int64_t)2 * block_size * num_kv_heads * head_dim * elem_bytes(kv_dtype) > (int64_t)UINT32_MAX)
         return PA_ERR_BAD_SHAPE;
     const int group = num_heads / num_kv_heads;
-    if (prefill_grid(num_seqs, num_kv_heads, group, max_new_tokens) > (int64_t)INT32_MAX) return PA_ERR_BAD_SHAPE;
+    if (prefill_grid(num_seqs, num_kv_heads, group, max_new_tokens, num_tokens) > (int64_t)INT32_MAX)
+        return PA_ERR_BAD_SHAPE;
     if (num_seqs == 0 || num_tokens == 0 || max_new_tokens == 0) return PA_OK;
     if (!cu_seqlens) return PA_ERR_NULL_POINTER;
     if (!aligned16(cu_seqlens)) return PA_ERR_MISALIGNED;
@@ -389,6 +390,7 @@ static pa_status prefill_impl(void* out, const void* query, pa_dtype q_dtype, co
     a.block_shift = log2_exact(block_size);
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_blocks = num_blocks;
+    a.max_new_tokens = max_new_tokens;
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;
     a.new_key = new_key;

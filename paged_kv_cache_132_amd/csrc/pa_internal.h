@@ -130,6 +130,7 @@ struct PrefillArgs {
     const int32_t* cu_seqlens;  // [num_seqs + 1]
     int32_t num_seqs, num_tokens, num_heads, num_kv_heads;
     int32_t block_size, block_shift, max_blocks_per_seq, num_blocks;
+    int32_t max_new_tokens;     // a sequence with more new tokens is skipped
     float score_scale;          // scale * k_scale * log2(e)
     float v_scale;
     // Fused prompt-stage write (null: none): the new tokens' K/V rows
@@ -181,7 +182,7 @@ int launch_decode_gqa16_mfma(const DecodeArgs& a, const DecodePlan& plan, pa_dty
 int launch_run_gqa16_mfma(const DecodeArgs& a, pa_dtype kv_dtype, void* stream);
 int launch_cache_write(const WriteArgs& a, pa_dtype src_dtype, pa_dtype kv_dtype, void* stream);
 int launch_copy_blocks(const CopyArgs& a, void* stream);
-int64_t prefill_grid(int num_seqs, int num_kv_heads, int group_size, int max_new_tokens);
+int64_t prefill_grid(int num_seqs, int num_kv_heads, int group_size, int max_new_tokens, int num_tokens);
 int launch_prefill(const PrefillArgs& a, pa_dtype kv_dtype, int head_dim, int group_size, int max_new_tokens,
                    void* stream);
 

@@ -25,13 +25,21 @@ def _start_pool(b):
     return poison_unused(pool, b.tables, b.context_lens, b.kv_dtype)
 
 
-def _gpu_prompt(b, pool_np):
+def _nan_out(b):
+    """An output buffer filled with NaN: a row the kernel never writes stays
+    non-finite."""
+    return dev16(np.full(b.query.shape, 0x7E00 if b.q_dtype == "f16" else 0x7FC0, dtype=np.uint16), b.q_dtype)
+
+
+def _gpu_prompt(b, pool_np, max_new_tokens=None):
     bt, lens, cu = dev_i32(b.block_table_array()), dev_i32(b.context_lens), dev_i32(b.cu_seqlens)
     dev = dev_pool(pool_np, b.kv_dtype)
     pa.cache_write_tokens(dev, dev16(b.new_key, b.src_dtype), dev16(b.new_value, b.src_dtype), bt, lens, cu,
                           b.k_scale, b.v_scale)
+    if max_new_tokens is None:
+        max_new_tokens = int(b.new_lens.max(initial=0))
     out = pa.prefill(dev16(b.query, b.q_dtype), dev, bt, lens, cu, b.scale, b.k_scale, b.v_scale,
-                     max_new_tokens=int(b.new_lens.max(initial=0)))
+                     max_new_tokens=max_new_tokens, out=_nan_out(b))
     torch.cuda.synchronize()
     return dev, out
 
@@ -118,20 +126,24 @@ def test_chunked_prompt_matches_one_shot():
 
 def test_packed_mixed_prompts_full_size_sampled():
     """The 8 packed prompts of 128..2048 tokens (5256 in all), 32 heads,
-    head_dim 128, fp16: the whole pool bit-exact after the write; attention
-    rows checked against the oracle at sampled positions of every sequence
-    (each sampled row is the oracle's one-query prefill at that position)."""
+    head_dim 128, fp16: the whole pool bit-exact after the write; every
+    output row written (the buffer starts as NaN); attention rows checked
+    against the oracle at sampled positions of every sequence, one in each
+    128-row tile at least (each sampled row is the oracle's one-query prefill
+    at that position)."""
     b = make_prefill_mixed()
     pool = _start_pool(b)
     dev, out = _gpu_prompt(b, pool)
     want_pool = _oracle_pool(b, pool)
     assert np.array_equal(host_bits(dev), want_pool)
     got = oracle.to_f64(host_bits(out), "f16")
+    assert np.isfinite(got).all(), "an output row was not written"
     rng = np.random.default_rng(72)
     bt = b.block_table_array()
     for s in range(b.num_seqs):
         n = int(b.new_lens[s])
-        picks = sorted(set([0, n - 1, n // 2] + list(rng.integers(0, n, size=5))))
+        per_tile = [min(n - 1, t + int(rng.integers(0, 128))) for t in range(0, n, 128)]
+        picks = sorted(set([0, n - 1, n // 2] + list(rng.integers(0, n, size=5)) + per_tile))
         for i in picks:
             j = int(b.cu_seqlens[s]) + i
             ref = oracle.paged_prefill(b.query[j:j + 1], "f16", want_pool, "f16", bt[s:s + 1],
@@ -228,3 +240,61 @@ def test_prefill_write_packed_mixed_prompts_full_size():
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(dev), host_bits(dev_sep))
     assert np.array_equal(host_bits(out), host_bits(out_sep))
+
+
+@pytest.mark.parametrize("qd,kvd,hq,hkv", [("bf16", "bf16", 16, 4), ("f16", "f16", 8, 8)])
+def test_many_prompts_every_row(qd, kvd, hq, hkv):
+    """130 prompts (more sequences than one wave has lanes, so the search for
+    each workgroup's job goes over several groups of 64), new tokens 0..40
+    after cached prefixes of 0..150, some prompts empty: every output row
+    against the oracle, and pa_prefill_write bit for bit the same."""
+    rng = np.random.default_rng(77)
+    S = 130
+    new = rng.integers(0, 41, size=S)
+    new[::9] = 0
+    lens = new + rng.integers(0, 151, size=S)
+    lens[lens == 0] = 1
+    b = make_prefill("many", 77, lens, new, hq, hkv, 128, 16, qd, kvd)
+    pool = _start_pool(b)
+    dev, out = _gpu_prompt(b, pool)
+    want_pool = _oracle_pool(b, pool)
+    assert np.array_equal(host_bits(dev), want_pool)
+    ref = oracle.paged_prefill(b.query, qd, want_pool, kvd, b.block_table_array(), b.context_lens,
+                               b.cu_seqlens, 16, b.scale, b.k_scale, b.v_scale)
+    assert_decode_close(oracle.to_f64(host_bits(out), qd), ref, b)
+    bt, lens_d, cu = dev_i32(b.block_table_array()), dev_i32(b.context_lens), dev_i32(b.cu_seqlens)
+    dev_w = dev_pool(pool, kvd)
+    out_w = pa.prefill(dev16(b.query, qd), dev_w, bt, lens_d, cu, b.scale, max_new_tokens=int(new.max()),
+                       new_key=dev16(b.new_key, qd), new_value=dev16(b.new_value, qd))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dev_w), host_bits(dev))
+    assert np.array_equal(host_bits(out_w), host_bits(out))
+
+
+def test_run_longer_than_max_new_tokens_is_skipped():
+    """A sequence with more new tokens than max_new_tokens is neither attended
+    nor (pa_prefill_write) written: its output rows keep what the buffer held
+    and its slots keep the pool's old values; the other sequences are
+    unaffected."""
+    b = make_prefill("cap", 78, [100, 50, 300], [100, 50, 80], 8, 8, 128, 16, "f16", "f16")
+    pool = _start_pool(b)
+    dev, out = _gpu_prompt(b, pool, max_new_tokens=80)
+    got = oracle.to_f64(host_bits(out), "f16")
+    skipped = slice(0, 100)
+    assert np.isnan(got[skipped]).all()
+    want_pool = _oracle_pool(b, pool)
+    ref = oracle.paged_prefill(b.query, "f16", want_pool, "f16", b.block_table_array(), b.context_lens,
+                               b.cu_seqlens, 16, b.scale)
+    assert_decode_close(got[100:], ref[100:], b)
+    # the fused write leaves sequence 0's new slots as they were
+    bt, lens_d, cu = dev_i32(b.block_table_array()), dev_i32(b.context_lens), dev_i32(b.cu_seqlens)
+    dev_w = dev_pool(pool, "f16")
+    out_w = pa.prefill(dev16(b.query, "f16"), dev_w, bt, lens_d, cu, b.scale, max_new_tokens=80,
+                       new_key=dev16(b.new_key, "f16"), new_value=dev16(b.new_value, "f16"), out=_nan_out(b))
+    torch.cuda.synchronize()
+    # the oracle's write of sequences 1 and 2 only (packed rows 100..229)
+    want_w = oracle.cache_write_tokens(pool, "f16", b.new_key[100:], b.new_value[100:], "f16",
+                                       b.block_table_array(), b.context_lens,
+                                       np.array([0, 0, 50, 130], dtype=np.int32), 16)
+    assert np.array_equal(host_bits(dev_w), want_w)
+    assert np.array_equal(host_bits(out_w), host_bits(out))
