@@ -10,11 +10,14 @@ each step reads its pool from HBM rather than from the 256 MB last-level
 cache.
 
 Steps run twice: eagerly, with HIP events around every launch (the per-kernel
-breakdown), and as replays of a HIP graph holding the same launches (the step
-time a decode loop sees once launch gaps are gone).  Each graph's output is
-checked against the eager output before timing.  A labelled warm figure
-(warm_ms_per_step) replays one graph on one pool copy, so caches may hold
-part of the pool.
+breakdown), and as replays of HIP graphs holding the same launches (the step
+time a decode loop sees once launch gaps are gone).  The pool copies stand
+for a model's layers: one graph holds the step of every copy in turn, as a
+model's decode graph holds every layer's attention, and the timed steps run
+through it; one graph per step (a graph launch between steps) is timed
+beside it.  Each graph's output is checked against the eager output before
+timing.  A labelled warm figure (warm_ms_per_step) replays one graph on one
+pool copy, so caches may hold part of the pool.
 
 Prints one JSON line:
   value       KV-read GB/s of the whole step (algorithmic bytes / graph-replayed
@@ -22,8 +25,9 @@ Prints one JSON line:
   roofline    the attention kernel's algorithmic bytes (the write's included
               when it is fused) / its mean duration from HIP events recorded
               around every launch in the timed region, against the 8 TB/s HBM
-              peak; the whole call (attention + split-K merge) is reported
-              beside it
+              peak; the whole call (attention + split-K merge, timed in a
+              loop of its own with no event between its two launches) is
+              reported beside it
   cpu_baseline  the float64 CPU oracle on the same batch (1 BLAS thread)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama7b]
@@ -466,8 +470,9 @@ def run_decode(args, torch, pa, b) -> dict:
     if run_size != 1 and not fused:
         raise SystemExit("--run-size takes the fused step (pa_decode_write_partials_shared)")
 
-    def step(i, ev=None):
+    def step(i, ev=None, split=True):
         # one pass of the hot path: cache write, attention pass, split-K merge.
+        # (split=False: no event between the two decode launches)
         # Fused (default): pa_decode_write_partials writes the newest token in
         # the attention pass; otherwise pa_cache_write runs first.
         pool = dev["pools"][i % copies]
@@ -483,7 +488,7 @@ def run_decode(args, torch, pa, b) -> dict:
             pa.decode(*dargs, phase="partials", new_key=dev["k"], new_value=dev["v"], run_size=run_size, **dkw)
         else:
             pa.decode(*dargs, phase="partials", **dkw)
-        if ev is not None:
+        if ev is not None and split:
             ev[2].record(stream)
         pa.decode(*dargs, phase="merge", **dkw)
         if ev is not None:
@@ -502,8 +507,14 @@ def run_decode(args, torch, pa, b) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     eager_ms_step = wall * 1e3 / args.steps
+    # the whole pa_decode call (attention pass + merge) timed on its own,
+    # without the event between its two launches
+    call_events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, call_events[i], split=False)
+    torch.cuda.synchronize()
 
-    graph_ms_step = warm_ms_step = None
+    graph_ms_step = warm_ms_step = graph_ms_step_one = None
     if not args.eager:
         # one graph per pool copy, each holding write + attention + merge
         ref = out.clone()
@@ -527,15 +538,48 @@ def run_decode(args, torch, pa, b) -> dict:
             torch.cuda.synchronize()
             if not torch.equal(out, ref):
                 raise RuntimeError(f"graph replay {c} differs from the eager step")
-        log(f"graph replay: {copies} graphs checked against the eager step")
+        # The pool copies stand for the layers of a model, whose decode graph
+        # holds every layer's attention back to back: one graph with the step
+        # of each copy in turn.  The timed steps run through it (and through
+        # the per-copy graphs for a remainder), so consecutive steps meet no
+        # graph-launch gap; one graph per step is timed beside it.
+        layers = torch.cuda.CUDAGraph()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(layers, stream=side):
+                for c in range(copies):
+                    step(c)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        out.zero_()
+        layers.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("the graph of all pool copies differs from the eager step")
+        log(f"graph replay: {copies} graphs and the graph of all {copies} copies checked against the eager step")
+
+        def timed(run_steps):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            run_steps()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t) * 1e3 / args.steps
+
+        def through_layers():
+            for _ in range(args.steps // copies):
+                layers.replay()
+            for i in range(args.steps % copies):
+                graphs[i].replay()
+
+        def one_per_graph():
+            for i in range(args.steps):
+                graphs[(args.warmup + i) % copies].replay()
+
         for i in range(args.warmup):
             graphs[i % copies].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[(args.warmup + i) % copies].replay()
-        torch.cuda.synchronize()
-        graph_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        layers.replay()
+        graph_ms_step = timed(through_layers)
+        graph_ms_step_one = timed(one_per_graph)
         # labelled warm figure: every step on the same pool copy, so the L2s
         # and the MALL may still hold part of it from the step before
         t0 = time.perf_counter()
@@ -543,12 +587,12 @@ def run_decode(args, torch, pa, b) -> dict:
             graphs[0].replay()
         torch.cuda.synchronize()
         warm_ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        del graphs
+        del graphs, layers
 
     write_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     attn_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     merge_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
-    call_ms = np.array([e[1].elapsed_time(e[3]) for e in events])
+    call_ms = np.array([e[1].elapsed_time(e[3]) for e in call_events])
     ms_step = graph_ms_step if graph_ms_step is not None else eager_ms_step
     attn_us = float(attn_ms.mean() * 1e3)
     call_us = float(call_ms.mean() * 1e3)
@@ -566,7 +610,8 @@ def run_decode(args, torch, pa, b) -> dict:
         f"pa_decode call {call_us:.1f} us; "
         f"{'write fused' if fused else f'write {write_ms.mean() * 1e3:.1f} us'}; eager step "
         f"{eager_ms_step * 1e3:.1f} us; graph step "
-        f"{'-' if graph_ms_step is None else f'{graph_ms_step * 1e3:.1f}'} us")
+        f"{'-' if graph_ms_step is None else f'{graph_ms_step * 1e3:.1f}'} us "
+        f"({'-' if graph_ms_step_one is None else f'{graph_ms_step_one * 1e3:.1f}'} us with one graph per step)")
     traffic = counter_traffic(b.name, partition, fused, run_size)
     achievable = stream_read_gbs(torch)
     log(f"streaming-read kernel reaches {achievable:.0f} GB/s on this device")
@@ -593,6 +638,10 @@ def run_decode(args, torch, pa, b) -> dict:
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_launch": "hip_graph" if graph_ms_step is not None else "eager",
         "warm_ms_per_step": round(warm_ms_step, 4) if graph_ms_step is not None else None,
+        "graph": (f"one graph holding the steps of all {copies} pool copies (the layers of a model) "
+                  "in turn" if graph_ms_step is not None else None),
+        "graph_ms_per_step_one_graph_per_step": (round(graph_ms_step_one, 4)
+                                                  if graph_ms_step_one is not None else None),
         "step_kernels": (f"pa_decode_write_partials_shared (runs of {run_size}, cache write fused), "
                          "pa_decode_merge" if run_size != 1 else
                          "pa_decode_write_partials (cache write fused), pa_decode_merge" if fused else
