@@ -155,43 +155,67 @@ __device__ __forceinline__ int cached_at(const int (&v)[kCachedChunks], int s) {
 // Token chunks (partition 0, the library's choice).
 //
 // The sequences' tokens are laid end to end, each sequence padded to whole
-// blocks (`units` blocks in all), and cut at block boundaries into N chunks
-// of near-equal length: chunk c holds blocks [c*units/N, (c+1)*units/N).  N
-// is the number of workgroup slots the GPU holds at once divided among the
+// blocks and preceded by a head of seg_head tokens that holds no work
+// (`units` blocks in all), and cut at block boundaries into N chunks of
+// near-equal length: chunk c holds blocks [c*units/N, (c+1)*units/N).  N is
+// the number of workgroup slots the GPU holds at once divided among the
 // KV-head groups, so that every workgroup starts in the first dispatch round
-// and every compute unit is dealt about the same number of tokens -- a
-// compute unit streams at about a fixed rate, so it is the tokens per unit,
-// not per workgroup, that decide when the last one finishes.  Chunks are not
-// shorter than part_min tokens, so small batches take fewer of them.  A
-// chunk covers the end of one sequence, whole sequences, and the start of
-// another, each a segment; a segment that is not its sequence's whole range
-// leaves a partial result for the merge, in slot 2c (the chunk's first
-// segment) or 2c + 1 (its last), which no other segment of the chunk can
-// need.
+// and every compute unit is dealt about the same work -- a compute unit
+// streams at about a fixed rate, so it is the work per unit, not per
+// workgroup, that decides when the last one finishes.  The heads make that
+// work more than tokens: each sequence a workgroup starts costs it the round
+// trips of a fresh start (length, query, table, first K/V), so a chunk with
+// many short sequences takes fewer tokens.  Chunks are not shorter than
+// part_min tokens, so small batches take fewer of them.  A chunk covers the
+// end of one sequence, whole sequences, and the start of another, each a
+// segment; a segment that is not its sequence's whole range leaves a partial
+// result for the merge, in slot 2c (the chunk's first segment) or 2c + 1
+// (its last), which no other segment of the chunk can need.
+
+// Segment of sequence w.s (layout offset w.off, its tokens from seg_head on)
+// that chunk [pos, end) holds: tokens [t0, t1); false when it holds none.
+// An empty sequence counts its one padded block.
+__device__ __forceinline__ bool chunk_segment(const DecodeArgs& a, WorkItem& w) {
+    const int r0 = w.off + a.seg_head;
+    w.t0 = max(w.pos - r0, 0);
+    w.t1 = min(w.L, w.end - r0);
+    return r0 < w.end && r0 + max(w.L, 1) > w.pos;
+}
+
+// On to the sequence after w.s, if its layout starts inside the chunk.
+__device__ __forceinline__ bool next_chunk_sequence(const DecodeArgs& a, WorkItem& w) {
+    w.off += a.seg_head + padded_len(w.L, a.block_size);
+    ++w.s;
+    if (w.off >= w.end || w.s >= a.num_seqs) return false;
+    w.L_raw = a.context_lens[w.s];
+    w.L = min(w.L_raw, a.max_blocks_per_seq << a.block_shift);
+    return true;
+}
 
 __device__ inline bool begin_chunk_work(const DecodeArgs& a, int wg, WorkItem& w) {
     const int lane = threadIdx.x & 63;
     const int B = a.num_seqs;
     const int U = a.block_size;
+    const int E = a.seg_head;
     const int max_tokens = a.max_blocks_per_seq << a.block_shift;
     int len_raw[kCachedChunks], padded[kCachedChunks];
     load_lengths(a, len_raw);
 #pragma unroll
     for (int i = 0; i < kCachedChunks; ++i)
-        padded[i] = lane + 64 * i < B ? padded_len(min(len_raw[i], max_tokens), U) : 0;
-    // padded tokens of sequences [0, s): every wave computes the same sums
+        padded[i] = lane + 64 * i < B ? E + padded_len(min(len_raw[i], max_tokens), U) : 0;
+    // layout tokens of sequences [0, s): every wave computes the same sums
     auto offset_of = [&](int s) {
         int acc = 0;
 #pragma unroll
         for (int i = 0; i < kCachedChunks; ++i) acc += lane + 64 * i < s ? padded[i] : 0;
         for (int x = lane + 64 * kCachedChunks; x < s; x += 64)
-            acc += padded_len(min(a.context_lens[x], max_tokens), U);
+            acc += E + padded_len(min(a.context_lens[x], max_tokens), U);
         return wave_total(acc);
     };
     const int total = offset_of(B);
     const int units = total / U;
     const int slots = max(a.target_items / a.groups, 1);
-    const int n = max(1, min(min(slots, (total + a.part_min - 1) / a.part_min), units));
+    const int n = max(1, min(min(min(slots, (total + a.part_min - 1) / a.part_min), units), a.max_chunks));
     const int items = n * a.groups;
     if (wg >= items) return false;
     // The hardware deals workgroup ids round-robin to the XCDs (id % kXcds);
@@ -222,24 +246,20 @@ __device__ inline bool begin_chunk_work(const DecodeArgs& a, int wg, WorkItem& w
     w.L = min(w.L_raw, max_tokens);
     w.p = 0;
     w.n_part = 0;
-    w.t0 = w.pos - w.off;
-    w.t1 = min(w.L, w.end - w.off);
     w.seg_slot = 2 * (int64_t)w.chunk;
+    // the chunk's first segment: that sequence's, unless the chunk starts
+    // past its tokens (in its last block's padding) or in the head of the next
+    while (!chunk_segment(a, w))
+        if (!next_chunk_sequence(a, w)) return false;
     return true;
 }
 
-// The next sequence of the chunk, if the chunk reaches it.  Its length is
-// loaded here, together with whatever the segment loads next.
+// The next sequence of the chunk, if the chunk holds some of its tokens.
+// Its length is loaded here, together with whatever the segment loads next.
 __device__ inline bool next_chunk_segment(const DecodeArgs& a, WorkItem& w) {
-    w.off += padded_len(w.L, a.block_size);
-    ++w.s;
-    if (w.off >= w.end || w.s >= a.num_seqs) return false;
-    w.L_raw = a.context_lens[w.s];
-    w.L = min(w.L_raw, a.max_blocks_per_seq << a.block_shift);
-    w.t0 = 0;
-    w.t1 = min(w.L, w.end - w.off);
+    if (!next_chunk_sequence(a, w)) return false;
     w.seg_slot = 2 * (int64_t)w.chunk + 1;
-    return true;
+    return chunk_segment(a, w);
 }
 
 // ---------------------------------------------------------------------------

@@ -501,6 +501,18 @@ pa_status pa_copy_blocks(const void* src_pool, int32_t src_num_blocks, void* dst
 }  // extern "C"
 
 namespace pa {
+// Token chunks: the head laid ahead of each sequence in the layout, in
+// tokens (rounded up to whole blocks): about what a workgroup streams in the
+// time a fresh segment start costs it, per kernel.
+constexpr int kSegHeadVector = 64;
+constexpr int kSegHeadMfma16 = 64;
+constexpr int kSegHeadFp8 = 160;
+
+int seg_head_tokens(const DecodePlan& p, pa_dtype kv_dtype, int block_size) {
+    const int t = !p.geo.mfma ? kSegHeadVector : kv_dtype == PA_FP8_E4M3 ? kSegHeadFp8 : kSegHeadMfma16;
+    return (t + block_size - 1) / block_size * block_size;
+}
+
 pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dtype, const void* kv_pool,
                         pa_dtype kv_dtype, const int32_t* block_tables, const int32_t* context_lens,
                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -549,6 +561,7 @@ pa_status decode_phases(int phases, void* out, const void* query, pa_dtype q_dty
     a.max_chunks = plan.max_chunks;
     a.target_items = plan.max_chunks * plan.groups;    // the launcher sets it from the kernel's occupancy
     a.fallback_partition = plan.run_partition;
+    a.seg_head = seg_head_tokens(plan, kv_dtype, block_size);
     a.score_scale = scale * (fp8 ? k_scale : 1.0f) * 1.4426950408889634f;
     a.v_scale = fp8 ? v_scale : 1.0f;
     a.new_key = new_key;

@@ -92,6 +92,9 @@ struct DecodeArgs {
     // partition 0 with a batch that shares prefix blocks, or shared runs:
     // the fixed partition taken instead
     int32_t fallback_partition;
+    // token chunks: tokens of layout laid ahead of every sequence (a whole
+    // number of blocks, no work), standing for what starting a segment costs
+    int32_t seg_head;
     float score_scale;      // scale * k_scale * log2(e): scores in the exp2 domain
     float v_scale;
     // Fused cache write (null: none): the newest token's K/V rows
