@@ -484,14 +484,15 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-            if (i0 + k >= list.n) break;                // uniform: one sequence per workgroup
-            const float m_new = fmaxf(M, mp[k]);
-            const float alpha = fast_exp2(M - m_new);   // 0 on the first partial
-            const float f = fast_exp2(mp[k] - m_new);
-            den = fmaf(den, alpha, f * lp[k]);
+            if (i0 + k < list.n) {                      // uniform: one sequence per workgroup
+                const float m_new = fmaxf(M, mp[k]);
+                const float alpha = fast_exp2(M - m_new);   // 0 on the first partial
+                const float f = fast_exp2(mp[k] - m_new);
+                den = fmaf(den, alpha, f * lp[k]);
 #pragma unroll
-            for (int e = 0; e < NE; ++e) num[e] = fmaf(num[e], alpha, f * op[k][e]);
-            M = m_new;
+                for (int e = 0; e < NE; ++e) num[e] = fmaf(num[e], alpha, f * op[k][e]);
+                M = m_new;
+            }
         }
     }
     const float inv = a.v_scale / den;
