@@ -114,9 +114,11 @@ bool plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
         if (part < block_size) part = block_size;
         p.run_partition = (part + block_size - 1) / block_size * block_size;
     }
-    // token chunks: at least 64 tokens (whole blocks) each, never more chunks
+    // token chunks: at least 128 tokens (whole blocks) each, never more chunks
     // than the GPU holds workgroups at once, nor than the batch's tokens fill
-    p.part_min = (64 + block_size - 1) / block_size * block_size;
+    // (a batch too small to fill the GPU then leaves fewer partials for the
+    // merge; 64-token chunks were slower there, 256 too few for the 7B batch)
+    p.part_min = (128 + block_size - 1) / block_size * block_size;
     {
         const int64_t by_slots = std::max<int64_t>(1, (int64_t)device_cus() * p.geo.max_per_cu / p.groups);
         const int64_t by_tokens = std::max<int64_t>(1, ((int64_t)num_seqs * max_tokens + p.part_min - 1) / p.part_min);

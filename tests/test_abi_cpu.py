@@ -170,11 +170,11 @@ def test_write_zero_sequences_is_a_noop(lib):
 
 def test_workspace_and_partition_plan(lib):
     # 7B shape: 32 seqs, 32/32 heads, D 128, bs 16, up to 2048 tokens.
-    # Token chunks (partition 0): at least 64 tokens each; room for two
+    # Token chunks (partition 0): at least 128 tokens each; room for two
     # partials per chunk, at most 8 resident workgroups per compute unit of
     # the device (2048 without one), split among the 8 groups of 4 KV heads
     pt = pa.decode_partition_size(32, 32, 32, 128, 16, 128, F16)
-    assert pt == 64
+    assert pt == 128
     ws = pa.decode_workspace_size(32, 32, 32, 128, 16, 128, F16)
     slots = 2 * (2048 // 8)
     need = 32 * 4 * 4 + slots * 32 * 2 * 4 + slots * 32 * 128 * 4
