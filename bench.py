@@ -89,10 +89,11 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(config: str, partition: int, fused: bool, run_size: int = 1):
+def counter_traffic(config: str, partition, fused: bool, run_size: int = 1):
     """HBM bytes per attention launch from committed rocprofv3 counter runs, if
-    they were taken on the current decode sources, partition and step form
-    (cache write fused or separate, shared runs); otherwise None."""
+    they were taken on the current decode sources, split (a fixed partition in
+    tokens, or the token-chunk label the bench prints) and step form (cache
+    write fused or separate, shared runs); otherwise None."""
     path = os.path.join(REPO, "profiles", f"decode_{config}_traffic.json")
     if not os.path.exists(path):
         return None
